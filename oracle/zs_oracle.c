@@ -1,0 +1,260 @@
+/*
+ * zs_oracle.c -- CPU oracle of the sharded AdamW step (test infrastructure
+ * only; see zs_oracle.h for the citation keys and the floating-point
+ * contract).  Single-threaded and deliberately plain: every loop walks its
+ * elements in ascending order and every expression is written in the order
+ * the pages write it.  Build: gcc -O2 -ffp-contract=off -fno-fast-math.
+ */
+#include "zs_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- layout --------------------------------------------------------------- */
+
+int or_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align,
+              int32_t stage, int64_t* shard_len, int64_t* shard_offset,
+              int64_t* valid_len)
+{
+    if (psi <= 0) return -1;
+    if (n_d < 1) return -2;
+    if (rank < 0 || rank >= n_d) return -3;
+    if (align < 1) return -4;
+    if (stage < 0 || stage > 3) return -5;
+
+    int64_t S, off, V;
+    if (stage == 0) {
+        /* DDP: nothing is sharded, the whole vector is this rank's. */
+        S = ((psi + align - 1) / align) * align;
+        off = 0;
+        V = psi;
+    } else {
+        int64_t chunk = (psi + n_d - 1) / n_d;          /* ceil(psi / n_d)  */
+        S = ((chunk + align - 1) / align) * align;      /* round up to align */
+        off = (int64_t)rank * S;
+        V = psi - off;
+        if (V < 0) V = 0;
+        if (V > S) V = S;
+    }
+    *shard_len = S;
+    *shard_offset = off;
+    *valid_len = V;
+    return 0;
+}
+
+/* ---- accounting ----------------------------------------------------------- */
+
+double or_state_bytes(double psi, int32_t n_d, int32_t stage, double K)
+{
+    switch (stage) {
+    case 0: return (4.0 + K) * psi;
+    case 1: return 4.0 * psi + K * psi / n_d;
+    case 2: return 2.0 * psi + (2.0 + K) * psi / n_d;
+    case 3: return (4.0 + K) * psi / n_d;
+    default: return -1.0;
+    }
+}
+
+double or_comm_elems(double psi, int32_t stage)
+{
+    switch (stage) {
+    case 0: case 1: case 2: return 2.0 * psi;
+    case 3: return 3.0 * psi;
+    default: return -1.0;
+    }
+}
+
+double or_comm_bytes(double psi, int32_t n_d, int32_t stage,
+                     double bytes_per_elem)
+{
+    double e = or_comm_elems(psi, stage);
+    if (e < 0) return -1.0;
+    return e * bytes_per_elem * (double)(n_d - 1) / (double)n_d;
+}
+
+double or_comm_elems_accum(double psi, int32_t stage, int32_t m)
+{
+    switch (stage) {
+    case 0: case 1: return 2.0 * psi;
+    case 2: return m * psi + psi;
+    case 3: return 3.0 * m * psi;
+    default: return -1.0;
+    }
+}
+
+double or_hsdp_state_bytes(double psi, int32_t g, double K)
+{
+    return (4.0 + K) * psi / g;
+}
+
+double or_hsdp_intra_bytes(double psi, int32_t g, double bytes_per_elem)
+{
+    return 3.0 * bytes_per_elem * psi * (double)(g - 1) / (double)g;
+}
+
+double or_hsdp_inter_bytes(double psi, int32_t n_d, int32_t g,
+                           double bytes_per_elem)
+{
+    double r = (double)n_d / (double)g;
+    double shard = bytes_per_elem * psi / g;
+    return 2.0 * (r - 1.0) / r * shard;
+}
+
+/* ---- bfloat16 ------------------------------------------------------------- */
+
+static uint32_t f32_bits(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+static float bits_f32(uint32_t u) { float x; memcpy(&x, &u, 4); return x; }
+
+uint16_t or_bf16_rne(float x)
+{
+    uint32_t u = f32_bits(x);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);   /* NaN */
+    uint32_t hi = u >> 16;          /* kept: sign, exponent, 7 mantissa bits */
+    uint32_t lo = u & 0xFFFFu;      /* dropped bits */
+    /* Nearest; on an exact tie pick the even kept value.  A carry out of the
+     * mantissa moves to the next binade (or to Inf), which is the correct
+     * rounded result. */
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
+        hi += 1u;
+    return (uint16_t)hi;
+}
+
+float or_bf16_to_f32(uint16_t h)
+{
+    return bits_f32((uint32_t)h << 16);
+}
+
+void or_bf16_rne_array(const float* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = or_bf16_rne(x[i]);
+}
+
+/* ---- O1 ---------------------------------------------------------------- */
+
+void or_reduce_mean(int32_t n_d, const uint16_t* const* slices, int64_t n,
+                    float* g_out)
+{
+    const float nd = (float)n_d;
+    for (int64_t i = 0; i < n; ++i) {
+        float s = or_bf16_to_f32(slices[0][i]);
+        for (int32_t r = 1; r < n_d; ++r)
+            s = s + or_bf16_to_f32(slices[r][i]);
+        g_out[i] = s / nd;
+    }
+}
+
+/* ---- O2 / O3 -------------------------------------------------------------- */
+
+double or_sqnorm_accum(double q, const float* g, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double x = (double)g[i];
+        q = q + x * x;
+    }
+    return q;
+}
+
+float or_clip_coef(double Q, double max_norm)
+{
+    double c = max_norm / (sqrt(Q) + 1e-6);
+    if (c > 1.0) c = 1.0;           /* NaN fails the test and stays NaN */
+    return (float)c;
+}
+
+/* ---- O4 ------------------------------------------------------------------- */
+
+void or_make_consts(const or_hparams* h, or_consts* c)
+{
+    double t = (double)h->step;
+    c->b1 = (float)h->beta1;
+    c->b2 = (float)h->beta2;
+    c->c1 = (float)(1.0 - h->beta1);
+    c->c2 = (float)(1.0 - h->beta2);
+    c->bc1 = (float)(1.0 - pow(h->beta1, t));
+    c->bc2 = (float)(1.0 - pow(h->beta2, t));
+    c->lr = (float)h->lr;
+    c->wd = (float)h->weight_decay;
+    c->eps = (float)h->eps;
+}
+
+void or_adamw_f32(const or_consts* c, int64_t n, const float* g,
+                  int use_coef, float coef, float* w, float* m, float* v)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = g[i];
+        if (use_coef) gi = gi * coef;
+        float mi = (c->b1 * m[i]) + (c->c1 * gi);
+        float vi = (c->b2 * v[i]) + ((c->c2 * gi) * gi);
+        float mh = mi / c->bc1;
+        float vh = vi / c->bc2;
+        float u = (mh / (sqrtf(vh) + c->eps)) + (c->wd * w[i]);
+        w[i] = w[i] - (c->lr * u);
+        m[i] = mi;
+        v[i] = vi;
+    }
+}
+
+/* ---- O5 ------------------------------------------------------------------- */
+
+void or_pack(int64_t shard_len, int64_t valid_len, const float* w,
+             uint16_t* out)
+{
+    for (int64_t i = 0; i < valid_len; ++i) out[i] = or_bf16_rne(w[i]);
+    for (int64_t i = valid_len; i < shard_len; ++i) out[i] = 0;
+}
+
+/* ---- whole shard step ------------------------------------------------------ */
+
+int or_shard_step(int32_t n_d, int64_t shard_len, int64_t valid_len,
+                  const or_hparams* h, const uint16_t* const* slices,
+                  double other_sqnorm, float* w, float* m, float* v,
+                  uint16_t* out, double* local_sqnorm_out, float* coef_out)
+{
+    float* g = NULL;
+    if (valid_len > 0) {
+        g = (float*)malloc((size_t)valid_len * sizeof(float));
+        if (!g) return -1;
+        or_reduce_mean(n_d, slices, valid_len, g);
+    }
+    int clip = h->max_grad_norm > 0.0;
+    double q = or_sqnorm_accum(0.0, g, valid_len);
+    float coef = 1.0f;
+    if (clip) coef = or_clip_coef(q + other_sqnorm, h->max_grad_norm);
+    or_consts c;
+    or_make_consts(h, &c);
+    if (valid_len > 0) or_adamw_f32(&c, valid_len, g, clip, coef, w, m, v);
+    or_pack(shard_len, valid_len, w, out);
+    if (local_sqnorm_out) *local_sqnorm_out = q;
+    if (coef_out) *coef_out = coef;
+    free(g);
+    return 0;
+}
+
+/* ---- fp64 mode ------------------------------------------------------------- */
+
+void or_reduce_mean_f64(int32_t n_d, const double* const* slices, int64_t n,
+                        double* g_out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double s = slices[0][i];
+        for (int32_t r = 1; r < n_d; ++r) s = s + slices[r][i];
+        g_out[i] = s / (double)n_d;
+    }
+}
+
+void or_adamw_f64(const or_hparams* h, int64_t n, const double* g,
+                  double* w, double* m, double* v)
+{
+    double b1 = h->beta1, b2 = h->beta2, t = (double)h->step;
+    double bc1 = 1.0 - pow(b1, t), bc2 = 1.0 - pow(b2, t);
+    for (int64_t i = 0; i < n; ++i) {
+        double mi = b1 * m[i] + (1.0 - b1) * g[i];
+        double vi = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
+        double mh = mi / bc1, vh = vi / bc2;
+        w[i] = w[i] - h->lr * (mh / (sqrt(vh) + h->eps) + h->weight_decay * w[i]);
+        m[i] = mi;
+        v[i] = vi;
+    }
+}
