@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's sharded AdamW step (ZeRO / FSDP) on MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch: the
+reduce-scatter's local reduction of the N_d ranks' bf16 gradient slices to
+an fp32 mean with this shard's squared norm (clip pass), then the fused
+clip + AdamW + bf16 cast/pack into the all-gather slot.  Inputs are drawn by
+the seeded generator directly in HBM before timing starts.
+
+Default workload: one GPU's ZeRO-2 shard of a 7B model over 8 ranks (875M
+parameters, 8 bf16 gradient slices, global clip 1.0, t = 1000).
+
+Prints ONE JSON line.  Only one GPU is supported: --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "G params/s and achieved HBM GB/s (% of peak) for one shard's AdamW step"
+KERNEL_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_zero_amd", "csrc", "zs_kernels.hip")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed PMC
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"k_step_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        p = json.load(f)
+    if p.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    return p.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(wl, shard, seconds: float):
+    """The oracle as it stands (single thread) on a bounded sample of the same
+    shard: O1..O5 over consecutive 4M-parameter chunks until `seconds` of
+    oracle time; input generation is not timed."""
+    import numpy as np
+
+    import oracle as O
+    import zsgen
+    from zsgen.workloads import (STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_MASTER,
+                                 grad_stream)
+
+    h = O.Hparams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                  weight_decay=wl.weight_decay, step=wl.t0, max_grad_norm=wl.max_grad_norm)
+    chunk = 1 << 22
+    done, spent, q = 0, 0.0, 0.0
+    off, V = shard.shard_offset, shard.valid_len
+    while spent < seconds and done < V:
+        n = min(chunk, V - done)
+        sl = [zsgen.host_bf16(wl.seed, grad_stream(0), r, wl.t0, wl.grad_sigma, off + done, n,
+                              p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
+              for r in range(wl.n_d)]
+        w = zsgen.host_f32(wl.seed, STREAM_MASTER, 0, 0, wl.master_sigma, off + done, n)
+        m = (np.zeros(n, np.float32) if wl.m_sigma is None else
+             zsgen.host_f32(wl.seed, STREAM_EXP_AVG, 0, 0, wl.m_sigma, off + done, n))
+        v = (np.zeros(n, np.float32) if wl.v_sigma is None else
+             zsgen.host_f32(wl.seed, STREAM_EXP_AVG_SQ, 0, 0, wl.v_sigma, off + done, n,
+                            absval=True))
+        t0 = time.perf_counter()
+        g = O.reduce_mean(sl)
+        q = O.sqnorm_accum(q, g)
+        coef = O.clip_coef(q, wl.max_grad_norm) if wl.max_grad_norm > 0 else None
+        O.adamw_f32(h, g, w, m, v, coef=coef)
+        O.pack(n, w)
+        spent += time.perf_counter() - t0
+        done += n
+    return {"value": done / spent / 1e9, "unit": "G params/s", "cores": 1, "kind": "oracle",
+            "sample": (f"oracle O1-O5 (rank-order mean of {wl.n_d} bf16 slices, fp64 "
+                       f"squared norm, clip, fp32 AdamW, bf16 pack) on the first {done:,} "
+                       f"of the {V:,} shard parameters of workload {wl.name}, single "
+                       f"thread, {spent:.1f} s of oracle time; input generation untimed"),
+            "seconds": spent}
+
+
+def copy_ceiling(torch, nbytes=4 << 30, reps=10):
+    """Practical HBM bandwidth of a plain 16-byte-vector copy (read+write)."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "fsdp_sharded_optimizer_zero_amd", "libzs_benchcopy.so"))
+    lib.zs_bench_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
+    lib.zs_bench_copy.restype = C.c_int
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    st = torch.cuda.current_stream()
+    n16 = nbytes // 16
+    blocks = 256 * 16
+    best = None
+    for _ in range(2):
+        assert lib.zs_bench_copy(src.data_ptr(), dst.data_ptr(), n16, blocks, st.cuda_stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        assert lib.zs_bench_copy(src.data_ptr(), dst.data_ptr(), n16, blocks, st.cuda_stream) == 0
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    best = 2 * nbytes / (ms / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": best, "bytes_each_way": nbytes, "ms": ms}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="zero2_7b")
+    ap.add_argument("--schedule", choices=["mean", "reread"], default="mean",
+                    help="clip schedule: store the fp32 mean (default) or re-read the slices")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's shard only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the multi-GPU exchange is not part of this build.",
+              flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import fsdp_sharded_optimizer_zero_amd as Z
+    from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
+    from zsgen.workloads import WORKLOADS
+
+    Z.lib()                     # fail loudly if the HIP library is missing
+    wl = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    run = ShardRun(wl, store_mean=(args.schedule == "mean") if wl.max_grad_norm > 0 else None)
+    run.fill_state()
+    run.fill_grads(wl.t0)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    t = wl.t0
+    for _ in range(args.warmup):
+        run.step(t, stream=stream.cuda_stream)
+        t += 1
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        if run.clip:
+            run.reduce_pass(stream=stream.cuda_stream)
+        ev[k][1].record(stream)
+        run.update_pass(t, stream=stream.cuda_stream)
+        ev[k][2].record(stream)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    red_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    upd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    span_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+    ms_per_step = wall / K * 1e3
+    params = run.V * run.units
+    red_b, upd_b = run.algorithmic_bytes()
+    step_gbps = (red_b + upd_b) / (ms_per_step / 1e3) / 1e9
+
+    # dominant kernel: the fused step (k_step), one launch per unit per step
+    if upd_ms >= red_ms or not run.clip:
+        kname = ("k_step (fp32 mean in, clip, AdamW, bf16 pack)" if run.clip and run.store_mean
+                 else "k_step (bf16 slices in, AdamW, bf16 pack)")
+        launch_ms = upd_ms / run.units
+        launch_bytes = upd_b / run.units
+    else:
+        kname = "k_reduce_sqnorm + k_sqnorm_final (rank-order mean, fp64 squared norm)"
+        launch_ms = red_ms / run.units
+        launch_bytes = red_b / run.units
+    achieved = launch_bytes / (launch_ms / 1e3) / 1e9
+    traffic = load_traffic(wl.name)
+
+    out = {
+        "metric": METRIC,
+        "value": params / (ms_per_step / 1e3) / 1e9,
+        "unit": "G params/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "psi": wl.psi, "n_d": wl.n_d, "rank": run.rank,
+                   "stage": wl.stage, "units": run.units, "shard_params": params,
+                   "max_grad_norm": wl.max_grad_norm,
+                   "schedule": ("stored-mean" if run.store_mean else "reread")
+                   if run.clip else "fused"},
+        "hbm_gbps": step_gbps,
+        "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "algorithmic_bytes_per_step": red_b + upd_b,
+        "kernel_ms": {"clip_pass": red_ms, "update_pass": upd_ms, "event_span_per_step": span_ms},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kname,
+                     "algorithmic_bytes_per_launch": launch_bytes, "launch_ms": launch_ms},
+        "kernel_src_sha": kernel_source_sha(),
+    }
+    if not args.no_copy_ceiling:
+        del run
+        torch.cuda.empty_cache()
+        out["copy_ceiling"] = copy_ceiling(torch)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, Z.zs_layout(
+            wl.psi, wl.n_d, wl.rank, wl.align, wl.stage,
+            Z.ZS_OUT_GATHER if wl.out_mode == "gather" else Z.ZS_OUT_SHARD), args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

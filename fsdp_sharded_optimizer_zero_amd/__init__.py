@@ -1,0 +1,178 @@
+"""MI355X sharded optimizer step (ZeRO-1/2/3, FSDP) -- Python binding.
+
+Argument marshalling only: every function forwards to the C ABI of
+``libzero_shard.so`` (declared in ``include/zero_shard.h``) with the same
+name.  PyTorch tensors serve as device memory and streams; all arithmetic
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing, importing the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
+
+ZS_OK = 0
+ZS_EINVAL_PSI = -1
+ZS_EINVAL_ND = -2
+ZS_EINVAL_RANK = -3
+ZS_EINVAL_LAYOUT = -4
+ZS_EALIGN = -5
+ZS_EINVAL_HPARAM = -6
+ZS_EINVAL_STAGE = -7
+ZS_ENULL = -8
+ZS_EUNSUPPORTED = -9
+ZS_EWORKSPACE = -10
+ZS_ELAUNCH = -11
+ZS_MAX_RANKS = 64
+ZS_OUT_GATHER = 0
+ZS_OUT_SHARD = 1
+
+
+class ZSError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {zs_strerror(code)} (code {code})")
+        self.code = code
+
+
+class zs_shard(C.Structure):
+    _fields_ = [("psi", C.c_int64), ("n_d", C.c_int32), ("rank", C.c_int32),
+                ("align", C.c_int64), ("shard_len", C.c_int64), ("shard_offset", C.c_int64),
+                ("valid_len", C.c_int64), ("stage", C.c_int32), ("out_mode", C.c_int32)]
+
+    def __repr__(self):
+        return ("zs_shard(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_)
+                + ")")
+
+
+class zs_adamw(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64),
+                ("max_grad_norm", C.c_double)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libzero_shard.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build(); "
+                              "there is no CPU fallback")
+        L = C.CDLL(LIB_PATH)
+        P, vp, i32, i64, f64 = C.POINTER, C.c_void_p, C.c_int32, C.c_int64, C.c_double
+        L.zs_layout.argtypes = [i64, i32, i32, i64, i32, i32, P(zs_shard)]
+        L.zs_layout.restype = C.c_int
+        L.zs_workspace_bytes.argtypes = [P(zs_shard)]
+        L.zs_workspace_bytes.restype = C.c_size_t
+        L.zs_state_bytes.argtypes = [f64, i32, i32, f64]
+        L.zs_state_bytes.restype = f64
+        L.zs_comm_bytes.argtypes = [f64, i32, i32, f64]
+        L.zs_comm_bytes.restype = f64
+        L.shard_grad_sqnorm.argtypes = [P(zs_shard), vp, vp, vp, C.c_size_t, vp, i32, vp]
+        L.shard_grad_sqnorm.restype = C.c_int
+        L.zero_shard_step.argtypes = [P(zs_shard), P(zs_adamw), vp, vp, vp, f64, vp, vp, vp,
+                                      vp, vp]
+        L.zero_shard_step.restype = C.c_int
+        L.shard_pack_gather.argtypes = [P(zs_shard), vp, vp, vp]
+        L.shard_pack_gather.restype = C.c_int
+        L.zs_strerror.argtypes = [C.c_int]
+        L.zs_strerror.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def zs_strerror(code: int) -> str:
+    return lib().zs_strerror(code).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != ZS_OK:
+        raise ZSError(rc, what)
+
+
+def _ptr(t):
+    """Device address of a tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _slices(grad_slices):
+    if grad_slices is None:
+        return None
+    arr = (C.c_void_p * len(grad_slices))(*[_ptr(g) for g in grad_slices])
+    return arr
+
+
+# ---- host calls ------------------------------------------------------------------
+
+def zs_layout(psi: int, n_d: int, rank: int, align: int, stage: int = 2,
+              out_mode: int = ZS_OUT_GATHER) -> zs_shard:
+    s = zs_shard()
+    _check(lib().zs_layout(psi, n_d, rank, align, stage, out_mode, C.byref(s)), "zs_layout")
+    return s
+
+
+def zs_workspace_bytes(s: zs_shard) -> int:
+    return lib().zs_workspace_bytes(C.byref(s))
+
+
+def zs_state_bytes(psi, n_d, stage, K=12.0) -> float:
+    return lib().zs_state_bytes(float(psi), n_d, stage, float(K))
+
+
+def zs_comm_bytes(psi, n_d, stage, bytes_per_elem=2.0) -> float:
+    return lib().zs_comm_bytes(float(psi), n_d, stage, float(bytes_per_elem))
+
+
+def adamw(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1,
+          max_grad_norm=0.0) -> zs_adamw:
+    return zs_adamw(lr, beta1, beta2, eps, weight_decay, int(step), max_grad_norm)
+
+
+# ---- device calls (enqueue on `stream`; torch tensors or raw addresses) ------------
+
+def shard_grad_sqnorm(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
+                      accumulate: bool = False, stream=None, workspace_bytes=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if hasattr(workspace, "numel") else zs_workspace_bytes(s))
+    _check(lib().shard_grad_sqnorm(C.byref(s), _slices(grad_slices), _ptr(mean_out),
+                                   _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
+                                   1 if accumulate else 0, _stream(stream)),
+           "shard_grad_sqnorm")
+
+
+def zero_shard_step(s: zs_shard, h: zs_adamw, grad_slices=None, mean_in=None, sqnorm=None,
+                    other_sqnorm: float = 0.0, master=None, exp_avg=None, exp_avg_sq=None,
+                    param_out=None, stream=None) -> None:
+    _check(lib().zero_shard_step(C.byref(s), C.byref(h), _slices(grad_slices), _ptr(mean_in),
+                                 _ptr(sqnorm), float(other_sqnorm), _ptr(master),
+                                 _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out),
+                                 _stream(stream)), "zero_shard_step")
+
+
+def shard_pack_gather(s: zs_shard, master, param_out, stream=None) -> None:
+    _check(lib().shard_pack_gather(C.byref(s), _ptr(master), _ptr(param_out),
+                                   _stream(stream)), "shard_pack_gather")
+
+
+def build(verbose: bool = False) -> str:
+    from . import _build
+    return _build.build(verbose)

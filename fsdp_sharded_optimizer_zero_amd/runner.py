@@ -1,0 +1,165 @@
+"""One GPU's share of a sharded optimizer step, driven through the C ABI.
+
+``ShardRun`` holds, in HBM, everything one rank needs for a step of its shard
+(per FSDP unit when there are several): the N_d ranks' bf16 gradient slices
+(the other ranks are simulated as extra buffers on this GPU), the fp32
+master/m/v shard, the fp32 mean (clip path), the bf16 all-gather buffer (or
+the rank's own bf16 shard) and the fp64 squared norm.  Inputs come from the
+seeded generator, written directly into device memory.  ``step()`` issues
+exactly the library calls of one optimizer step on one stream:
+
+* no clip:   zero_shard_step(grad_slices=...)                 per unit
+* clip:      shard_grad_sqnorm(...)                           per unit
+             (squared norms summed in unit order: the global norm of the
+             FSDP model; the other ranks' shards enter as other_sqnorm),
+             then zero_shard_step(mean_in=..., sqnorm=...)    per unit
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+import zsgen
+from zsgen.workloads import (STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_MASTER, Workload,
+                             grad_stream)
+
+from . import (ZS_OUT_GATHER, ZS_OUT_SHARD, adamw, shard_grad_sqnorm, zero_shard_step,
+               zs_layout, zs_workspace_bytes)
+
+
+def _empty(n, dtype, device):
+    # never a zero-size allocation: keeps every pointer non-NULL and aligned
+    return torch.empty(max(int(n), 8), dtype=dtype, device=device)
+
+
+@dataclass
+class Unit:
+    slices: torch.Tensor       # int16 [n_d, S] (row r = rank r's slice, V used)
+    w: torch.Tensor
+    m: torch.Tensor
+    v: torch.Tensor
+    mean: torch.Tensor | None
+    out: torch.Tensor          # int16 [n_d*S] (gather) or [S] (shard)
+
+
+class ShardRun:
+    def __init__(self, wl: Workload, rank: int | None = None, device: str = "cuda",
+                 units: int | None = None, store_mean: bool | None = None):
+        self.wl = wl
+        self.rank = wl.rank if rank is None else rank
+        self.units = wl.units if units is None else units
+        self.device = device
+        out_mode = ZS_OUT_GATHER if wl.out_mode == "gather" else ZS_OUT_SHARD
+        self.shard = zs_layout(wl.psi, wl.n_d, self.rank, wl.align, wl.stage, out_mode)
+        self.clip = wl.max_grad_norm > 0
+        # the clip needs the norm before any update: store the mean, read it back
+        self.store_mean = self.clip if store_mean is None else store_mean
+        S, V, nd = self.shard.shard_len, self.shard.valid_len, wl.n_d
+        out_len = nd * S if out_mode == ZS_OUT_GATHER else S
+        if wl.stage == 0 and out_mode == ZS_OUT_GATHER:
+            out_len = S
+        self.out_len = out_len
+        self.units_data = []
+        for _ in range(self.units):
+            self.units_data.append(Unit(
+                slices=torch.empty((nd, S), dtype=torch.int16, device=device),
+                w=_empty(V, torch.float32, device), m=_empty(V, torch.float32, device),
+                v=_empty(V, torch.float32, device),
+                mean=_empty(V, torch.float32, device) if self.store_mean else None,
+                out=torch.empty(out_len, dtype=torch.int16, device=device)))
+        self.workspace = torch.empty(zs_workspace_bytes(self.shard) // 8, dtype=torch.float64,
+                                     device=device)
+        self.sqnorm = torch.zeros(1, dtype=torch.float64, device=device)
+        self.t = wl.t0
+
+    # ---- inputs ------------------------------------------------------------------
+
+    @property
+    def V(self):
+        return self.shard.valid_len
+
+    def fill_state(self, out_fill: int | None = None):
+        wl, V, off = self.wl, self.V, self.shard.shard_offset
+        for u, d in enumerate(self.units_data):
+            if V > 0:
+                zsgen.dev_f32(d.w[:V], wl.seed, STREAM_MASTER, u, 0, wl.master_sigma, off)
+                if wl.m_sigma is None:
+                    d.m.zero_()
+                else:
+                    zsgen.dev_f32(d.m[:V], wl.seed, STREAM_EXP_AVG, u, 0, wl.m_sigma, off)
+                if wl.v_sigma is None:
+                    d.v.zero_()
+                else:
+                    zsgen.dev_f32(d.v[:V], wl.seed, STREAM_EXP_AVG_SQ, u, 0, wl.v_sigma, off,
+                                  absval=True)
+            if out_fill is not None:
+                d.out.fill_(out_fill)
+
+    def fill_grads(self, t: int):
+        wl, V, off = self.wl, self.V, self.shard.shard_offset
+        if V == 0:
+            return
+        for u, d in enumerate(self.units_data):
+            for r in range(wl.n_d):
+                zsgen.dev_bf16(d.slices[r, :V], wl.seed, grad_stream(u), r, t, wl.grad_sigma,
+                               off, p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
+
+    # ---- the step -------------------------------------------------------------------
+
+    def hparams(self, t: int):
+        wl = self.wl
+        return adamw(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                     weight_decay=wl.weight_decay, step=t, max_grad_norm=wl.max_grad_norm)
+
+    def slice_ptrs(self, d: Unit):
+        S = self.shard.shard_len
+        base = d.slices.data_ptr()
+        return [base + 2 * S * r for r in range(self.wl.n_d)]
+
+    def reduce_pass(self, stream=None):
+        for u, d in enumerate(self.units_data):
+            shard_grad_sqnorm(self.shard, self.slice_ptrs(d), d.mean, self.workspace,
+                              self.sqnorm, accumulate=u > 0, stream=stream)
+
+    def update_pass(self, t: int, other_sqnorm: float = 0.0, stream=None):
+        h = self.hparams(t)
+        for d in self.units_data:
+            if self.clip and self.store_mean:
+                zero_shard_step(self.shard, h, mean_in=d.mean, sqnorm=self.sqnorm,
+                                other_sqnorm=other_sqnorm, master=d.w, exp_avg=d.m,
+                                exp_avg_sq=d.v, param_out=d.out, stream=stream)
+            else:
+                zero_shard_step(self.shard, h, grad_slices=self.slice_ptrs(d),
+                                sqnorm=self.sqnorm if self.clip else None,
+                                other_sqnorm=other_sqnorm, master=d.w, exp_avg=d.m,
+                                exp_avg_sq=d.v, param_out=d.out, stream=stream)
+
+    def step(self, t: int | None = None, other_sqnorm: float = 0.0, stream=None):
+        """Enqueue one optimizer step of every unit at bias-correction step t."""
+        t = self.t if t is None else t
+        if self.clip:
+            self.reduce_pass(stream)
+        self.update_pass(t, other_sqnorm, stream)
+        self.t = t + 1
+
+    # ---- bytes the step must move (algorithmic, per step) -------------------------------
+
+    def algorithmic_bytes(self):
+        """(reduce-pass bytes, update-pass bytes) over all units.
+
+        reduce pass: N_d bf16 reads + fp32 mean write = 2 N_d + 4 B/param
+        update pass: mean read (or N_d bf16 reads) + 12 B state read + 12 B
+        state write + 2 B bf16 write; pads are written too (2 B each)."""
+        nd, V, S = self.wl.n_d, self.V, self.shard.shard_len
+        pads = S - V
+        if self.clip and self.store_mean:
+            red = (2 * nd + 4) * V
+            upd = (4 + 12 + 12 + 2) * V + 2 * pads
+        elif self.clip:
+            red = 2 * nd * V
+            upd = (2 * nd + 26) * V + 2 * pads
+        else:
+            red = 0
+            upd = (2 * nd + 26) * V + 2 * pads
+        return red * self.units, upd * self.units

@@ -1,0 +1,193 @@
+/*
+ * zero_shard.h -- C ABI of the MI355X sharded optimizer step.
+ *
+ * One GPU's share of the ZeRO-1/2/3 and FSDP optimizer step: the local
+ * reduction of the reduce-scatter (N_d ranks' bf16 gradient slices of this
+ * rank's shard into an fp32 mean), the squared gradient norm for a global
+ * clip, the elementwise mixed-precision AdamW update of the shard's fp32
+ * master weights and moments, and the bf16 cast and pack of the new shard
+ * into the buffer the all-gather fills.
+ *
+ * Sources (page title, then section):
+ *  - "Data parallelism, ZeRO and FSDP" (ML Systems, Lesson 8): section 2
+ *    "What is redundant" (AdamW is elementwise, so rank k owns and updates
+ *    slice k) and "The communication is already there" (reduce-scatter, the
+ *    update of slice k, then the all-gather of the new weights); section 3
+ *    Theorem "ZeRO memory and communication" (12 optimizer bytes per
+ *    parameter, the stages); "How FSDP implements ZeRO-3" step 1 (a unit's
+ *    flat parameter cut into N_d equal chunks) and step 4 (a normal
+ *    optimizer on the local shards); section 5 "In code" (the adamw of the
+ *    simulator, whose expression order this library follows); section 7
+ *    "Common mistakes" (a global clip needs the squared shard norms summed).
+ *  - "Distributed Training Basics -- DDP and FSDP": the clip at the update
+ *    boundary in its DDP reference program; the errors raised by its
+ *    state_bytes helper.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *    16-byte aligned, owned by the caller.  The library allocates nothing and
+ *    keeps no state between calls.
+ *  - bf16 values are passed as their uint16_t bit patterns.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue
+ *    work and return; results are ready after the caller synchronises the
+ *    stream.  A device fault surfaces at that synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; a call
+ *    that returns an error has enqueued nothing and written nothing.
+ *  - Return value: ZS_OK (0) or one of the negative codes below.  Nothing is
+ *    thrown across the ABI.
+ *  - Arithmetic: IEEE-754 fp32, round to nearest even, no fused
+ *    multiply-add, correctly rounded division and square root, subnormals
+ *    kept; the squared norm in fp64.  NaN and Inf propagate (no skipping).
+ *  - Outputs must not overlap inputs, except master/exp_avg/exp_avg_sq which
+ *    are updated in place.  Calls that write the same buffers must not run
+ *    concurrently on different streams.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+#define ZS_OK               0
+#define ZS_EINVAL_PSI     (-1)   /* psi <= 0 */
+#define ZS_EINVAL_ND      (-2)   /* n_d < 1 */
+#define ZS_EINVAL_RANK    (-3)   /* rank outside [0, n_d) */
+#define ZS_EINVAL_LAYOUT  (-4)   /* align < 1, or shard_len / shard_offset /
+                                    valid_len not those zs_layout gives */
+#define ZS_EALIGN         (-5)   /* a pointer not 16-byte aligned, or
+                                    shard_len not a multiple of 8 */
+#define ZS_EINVAL_HPARAM  (-6)   /* lr < 0, beta outside [0,1), eps <= 0,
+                                    weight_decay < 0, step < 1, or any
+                                    hyperparameter not finite */
+#define ZS_EINVAL_STAGE   (-7)   /* stage outside 0..3 or unknown out_mode */
+#define ZS_ENULL          (-8)   /* a required pointer is NULL, or both /
+                                    neither of grad_slices and mean_in */
+#define ZS_EUNSUPPORTED   (-9)   /* n_d > ZS_MAX_RANKS */
+#define ZS_EWORKSPACE    (-10)   /* workspace smaller than zs_workspace_bytes */
+#define ZS_ELAUNCH       (-11)   /* the HIP runtime rejected a kernel launch */
+
+#define ZS_MAX_RANKS 64          /* gradient slices one call can reduce */
+
+/* Where the new bf16 shard goes. */
+#define ZS_OUT_GATHER 0  /* param_out is the bf16[n_d * shard_len] all-gather
+                            buffer; this rank writes at shard_offset (stage 0:
+                            offset 0, the whole vector) */
+#define ZS_OUT_SHARD  1  /* param_out is this rank's own bf16[shard_len] */
+
+/* One rank's shard of a flat parameter vector of psi elements.
+ * Stages: 0 = DDP (nothing sharded: the rank owns the whole vector),
+ * 1 = ZeRO-1, 2 = ZeRO-2, 3 = ZeRO-3 / FSDP.  The stage does not change the
+ * arithmetic, only the layout (stage 0) and which out_mode is natural. */
+typedef struct zs_shard {
+    int64_t psi;           /* parameters in the flat vector (or FSDP unit) */
+    int32_t n_d;           /* data-parallel ranks */
+    int32_t rank;          /* k, the owner of this shard */
+    int64_t align;         /* shard_len is a multiple of this */
+    int64_t shard_len;     /* S: padded slice length */
+    int64_t shard_offset;  /* k*S (0 at stage 0) */
+    int64_t valid_len;     /* V = clamp(psi - k*S, 0, S): real parameters */
+    int32_t stage;         /* 0..3 */
+    int32_t out_mode;      /* ZS_OUT_GATHER or ZS_OUT_SHARD */
+} zs_shard;
+
+/* AdamW hyperparameters (decoupled weight decay inside the step, on every
+ * element), in double; rounded once to fp32 by the library. */
+typedef struct zs_adamw {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;          /* t >= 1, the bias-correction step; the caller
+                              increments it between calls */
+    double max_grad_norm;  /* > 0: clip the gradient to this global L2 norm;
+                              <= 0: no clip */
+} zs_adamw;
+
+/* Fill *out with the shard of `rank`.  The flat vector is padded at its tail
+ * to n_d*S with S = roundup(ceil(psi/n_d), align) (stage 0: S =
+ * roundup(psi, align), offset 0, valid_len psi); slot k is [k*S, (k+1)*S).
+ * Host only.  Errors: ZS_EINVAL_PSI/ND/RANK/LAYOUT(align < 1)/STAGE,
+ * ZS_ENULL (out). */
+int zs_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align, int32_t stage,
+              int32_t out_mode, zs_shard* out);
+
+/* Bytes of device workspace shard_grad_sqnorm needs (a few KB of fp64
+ * partial sums; the same for every shard).  Host only. */
+size_t zs_workspace_bytes(const zs_shard* s);
+
+/* Model-state bytes per GPU of the Theorem's table: weights and gradients
+ * 2 bytes each, K optimizer bytes per parameter.  stage 0: (4+K)psi,
+ * 1: 4psi + K psi/n_d, 2: 2psi + (2+K) psi/n_d, 3: (4+K) psi/n_d.
+ * Returns -1 for psi <= 0, n_d < 1 or an unknown stage.  Host only. */
+double zs_state_bytes(double psi, int32_t n_d, int32_t stage, double K);
+
+/* Bytes each GPU sends per step: 2psi elements for stages 0-2, 3psi for
+ * stage 3, times bytes_per_elem and (n_d-1)/n_d (ring collectives).
+ * Returns -1 on invalid arguments.  Host only. */
+double zs_comm_bytes(double psi, int32_t n_d, int32_t stage, double bytes_per_elem);
+
+/* Clip pass: the reduce-scatter's local reduction plus this shard's squared
+ * L2 norm.
+ *   grad_slices  host array of n_d device pointers; grad_slices[r] is rank
+ *                r's bf16 gradient for this shard, valid_len elements.
+ *   mean_out     device fp32[valid_len] or NULL.  If given, receives
+ *                g_i = (sum over r = 0..n_d-1 in rank order of the widened
+ *                bf16 values) / n_d.
+ *   workspace    device, >= zs_workspace_bytes(s) bytes, 16-byte aligned;
+ *                contents on entry are ignored.
+ *   sqnorm_out   device, one double: sum of (double)g_i^2 over the shard.
+ *                accumulate == 0 overwrites it; accumulate != 0 adds the
+ *                shard's value to it (for a norm over several FSDP units,
+ *                summed in call order).
+ * The fp64 sum is taken in a fixed tree order (run-to-run deterministic for
+ * one shape), not in ascending element order.  An empty shard (valid_len 0)
+ * contributes 0.  Errors: ZS_ENULL, ZS_EINVAL_*, ZS_EALIGN, ZS_EUNSUPPORTED,
+ * ZS_EWORKSPACE, ZS_ELAUNCH. */
+int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices, float* mean_out,
+                      void* workspace, size_t workspace_bytes, double* sqnorm_out,
+                      int32_t accumulate, void* stream);
+
+/* The fused optimizer step of this shard.  Exactly one gradient source:
+ *   grad_slices  host array of n_d device pointers to bf16[valid_len]
+ *                (reduced here, in rank order, as shard_grad_sqnorm does), or
+ *   mean_in      device fp32[valid_len], the mean from shard_grad_sqnorm.
+ * If h->max_grad_norm > 0: `sqnorm` (device, one double, this shard's or the
+ * accumulated squared norm) is required and the global squared norm is
+ * Q = *sqnorm + other_sqnorm (other_sqnorm stands for the scalar all-reduce
+ * of the other ranks' squared shard norms);
+ * coef = f32(min(1, max_grad_norm / (sqrt(Q) + 1e-6))) in double, NaN kept,
+ * and g = g * coef.  Otherwise `sqnorm` and other_sqnorm are ignored.
+ * Then, for i < valid_len, in this order and in fp32 (b1 = f32(beta1),
+ * c1 = f32(1 - beta1), bc1 = f32(1 - beta1^t), likewise b2, c2, bc2):
+ *   m' = (b1*m) + (c1*g);  v' = (b2*v) + ((c2*g)*g)
+ *   w' = w - lr*((m'/bc1) / (sqrt(v'/bc2) + eps) + wd*w)
+ * master/exp_avg/exp_avg_sq (fp32[valid_len]) are updated in place, and
+ * param_out receives bf16_rne(w') at its base (ZS_OUT_GATHER: param_out +
+ * shard_offset; ZS_OUT_SHARD: param_out) followed by +0 in the
+ * shard_len - valid_len pad positions.  Nothing beyond valid_len is read or
+ * written in the state or gradient buffers, and nothing outside this
+ * rank's slot of the gather buffer is written.  bf16_rne: round to nearest
+ * even; any NaN becomes sign|0x7FC0.
+ * Errors: ZS_ENULL, ZS_EINVAL_*, ZS_EALIGN, ZS_EUNSUPPORTED, ZS_ELAUNCH. */
+int zero_shard_step(const zs_shard* s, const zs_adamw* h, const uint16_t* const* grad_slices,
+                    const float* mean_in, const double* sqnorm, double other_sqnorm,
+                    float* master, float* exp_avg, float* exp_avg_sq, uint16_t* param_out,
+                    void* stream);
+
+/* Cast and pack only: param_out (placed as in zero_shard_step) receives
+ * bf16_rne(master[i]) for i < valid_len and +0 in the pads.  The step of
+ * the all-gather that needs no optimizer work (e.g. to publish weights after
+ * loading a checkpoint).  Errors: ZS_ENULL, ZS_EINVAL_*, ZS_EALIGN,
+ * ZS_ELAUNCH. */
+int shard_pack_gather(const zs_shard* s, const float* master, uint16_t* param_out,
+                      void* stream);
+
+/* Static description of an error code ("unknown error" otherwise). */
+const char* zs_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,191 @@
+"""Oracle-side helpers for the GPU parity tests.
+
+Every expected value here is computed by the CPU oracle (``oracle``) from
+inputs drawn by the HOST side of the seeded generator (``zsgen.host_*``);
+nothing here reads a value produced on the GPU.  The GPU side fills its own
+buffers with the device side of the same generator.
+"""
+from __future__ import annotations
+
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import oracle as O
+import zsgen
+from zsgen.workloads import (STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_MASTER, Workload,
+                             grad_stream)
+
+FLT_MIN = np.float32(1.1754944e-38)
+REL_BAR = 2e-6          # fp32 state: max relative error against the oracle
+BF16_ULP_BAR = 1        # bf16 params: max distance in units in the last place
+
+
+def log(msg):
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def hparams(wl: Workload, t: int) -> O.Hparams:
+    return O.Hparams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                     weight_decay=wl.weight_decay, step=t, max_grad_norm=wl.max_grad_norm)
+
+
+# ---- host inputs ----------------------------------------------------------------------
+
+def host_state(wl: Workload, unit: int, start: int, n: int):
+    w = zsgen.host_f32(wl.seed, STREAM_MASTER, unit, 0, wl.master_sigma, start, n)
+    m = (np.zeros(n, np.float32) if wl.m_sigma is None else
+         zsgen.host_f32(wl.seed, STREAM_EXP_AVG, unit, 0, wl.m_sigma, start, n))
+    v = (np.zeros(n, np.float32) if wl.v_sigma is None else
+         zsgen.host_f32(wl.seed, STREAM_EXP_AVG_SQ, unit, 0, wl.v_sigma, start, n,
+                        absval=True))
+    return w, m, v
+
+
+def host_state_at(wl: Workload, unit: int, idx):
+    w = zsgen.host_f32_at(wl.seed, STREAM_MASTER, unit, 0, wl.master_sigma, idx)
+    m = (np.zeros(len(idx), np.float32) if wl.m_sigma is None else
+         zsgen.host_f32_at(wl.seed, STREAM_EXP_AVG, unit, 0, wl.m_sigma, idx))
+    v = (np.zeros(len(idx), np.float32) if wl.v_sigma is None else
+         zsgen.host_f32_at(wl.seed, STREAM_EXP_AVG_SQ, unit, 0, wl.v_sigma, idx, absval=True))
+    return w, m, v
+
+
+def host_slices(wl: Workload, unit: int, t: int, start: int, n: int):
+    return [zsgen.host_bf16(wl.seed, grad_stream(unit), r, t, wl.grad_sigma, start, n,
+                            p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
+            for r in range(wl.n_d)]
+
+
+def host_slices_at(wl: Workload, unit: int, t: int, idx):
+    return [zsgen.host_bf16_at(wl.seed, grad_stream(unit), r, t, wl.grad_sigma, idx,
+                               p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
+            for r in range(wl.n_d)]
+
+
+# ---- oracle runs ----------------------------------------------------------------------
+
+def oracle_full_run(wl: Workload, rank: int, steps: int, t0: int, shard, other_sqnorm=0.0):
+    """Whole-shard oracle over `steps` steps.  Returns (w, m, v, slot_out, qs, coefs)."""
+    S, off, V = shard.shard_len, shard.shard_offset, shard.valid_len
+    w, m, v = host_state(wl, 0, off, V)
+    qs, coefs = [], []
+    out = None
+    for i in range(steps):
+        t = t0 + i
+        sl = host_slices(wl, 0, t, off, V)
+        out, q, coef = O.shard_step(wl.n_d, S, V, hparams(wl, t), sl, w, m, v,
+                                    other_sqnorm=other_sqnorm)
+        qs.append(q)
+        coefs.append(coef)
+    return w, m, v, out, qs, coefs
+
+
+def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
+                          chunk: int = 1 << 24, keep_idx=None):
+    """Oracle squared norm of the mean over [start, start+n), ascending, in
+    chunks (the accumulator is carried, so the order is the plain one).  The
+    host generator fills chunk k+1 while the oracle reduces chunk k.  If
+    keep_idx (sorted, relative to start) is given, also returns the oracle's
+    mean at those positions."""
+    q = 0.0
+    kept = np.empty(0 if keep_idx is None else len(keep_idx), np.float32)
+    starts = list(range(0, n, chunk))
+
+    def gen(a):
+        return host_slices(wl, unit, t, start + a, min(chunk, n - a))
+
+    with ThreadPoolExecutor(max_workers=1) as ex:
+        fut = ex.submit(gen, starts[0]) if starts else None
+        for ci, a in enumerate(starts):
+            sl = fut.result()
+            if ci + 1 < len(starts):
+                fut = ex.submit(gen, starts[ci + 1])
+            g = O.reduce_mean(sl)
+            q = O.sqnorm_accum(q, g)
+            if keep_idx is not None:
+                lo, hi = np.searchsorted(keep_idx, [a, a + len(g)])
+                kept[lo:hi] = g[keep_idx[lo:hi] - a]
+            if ci % 8 == 7:
+                log(f"  oracle sqnorm {wl.name} unit {unit}: {a + len(g):,}/{n:,}")
+    if keep_idx is not None:
+        return q, kept
+    return q
+
+
+def oracle_sampled_step(wl: Workload, unit: int, t: int, shard, idx, coef):
+    """Oracle O1, O4, O5 at shard positions idx (relative to the shard), given
+    the oracle's clip coefficient (None: no clip).  Returns (w, m, v, bf16)."""
+    gidx = shard.shard_offset + np.asarray(idx, np.int64)
+    sl = host_slices_at(wl, unit, t, gidx)
+    g = O.reduce_mean(sl)
+    w, m, v = host_state_at(wl, unit, gidx)
+    O.adamw_f32(hparams(wl, t), g, w, m, v, coef=coef)
+    return w, m, v, O.bf16_rne(w), g
+
+
+def sample_indices(V: int, n_random: int, seed: int, edge: int = 4096):
+    """Both ends of the shard plus uniform random positions, sorted, unique."""
+    if V == 0:
+        return np.zeros(0, np.int64)
+    rng = np.random.default_rng(seed)
+    parts = [np.arange(min(edge, V)), np.arange(max(0, V - edge), V),
+             rng.integers(0, V, size=n_random)]
+    return np.unique(np.concatenate(parts).astype(np.int64))
+
+
+# ---- comparisons ----------------------------------------------------------------------
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    got = got.astype(np.float64)
+    ref = ref.astype(np.float64)
+    both_nan = np.isnan(got) & np.isnan(ref)
+    err = np.abs(got - ref) / np.maximum(np.abs(ref), float(FLT_MIN))
+    err[both_nan] = 0.0
+    err[np.isnan(err)] = np.inf
+    same_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    err[same_inf] = 0.0
+    return err
+
+
+def bf16_ulp_dist(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in bf16 steps between two bf16 bit-pattern arrays (sign-magnitude
+    mapped to a monotone integer line)."""
+    def line(x):
+        x = x.astype(np.int64) & 0xFFFF
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(line(a) - line(b))
+
+
+def assert_state_close(name, got, ref):
+    e = rel_err(got, ref)
+    nbit = int(np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32)))
+    log(f"  {name}: max rel err {e.max() if e.size else 0:.3g}, non-bitwise {nbit}/{got.size}")
+    assert e.size == 0 or e.max() <= REL_BAR, f"{name}: max rel err {e.max()} > {REL_BAR}"
+    return nbit
+
+
+def assert_bf16_close(name, got, ref):
+    got = got.astype(np.uint16)
+    ref = ref.astype(np.uint16)
+    d = bf16_ulp_dist(got, ref)
+    nbit = int(np.count_nonzero(got != ref))
+    log(f"  {name}: max bf16 ulp {d.max() if d.size else 0}, non-bitwise {nbit}/{got.size}")
+    assert d.size == 0 or d.max() <= BF16_ULP_BAR
+    return nbit
+
+
+def coef_is_robust(Q: float, max_norm: float) -> bool:
+    """True if every Q' within 1e-12 relative of Q gives the same fp32 clip
+    coefficient (so the GPU's differently ordered fp64 sum cannot change it)."""
+    c = O.clip_coef(Q, max_norm)
+    return (O.clip_coef(Q * (1 - 1e-12), max_norm) == c and
+            O.clip_coef(Q * (1 + 1e-12), max_norm) == c)
+
+
+def gpu_threads_note():
+    return os.environ.get("OMP_NUM_THREADS", "")

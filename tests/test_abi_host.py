@@ -1,0 +1,181 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load and export every function include/zero_shard.h
+declares; its layout and accounting must agree with the oracle's independent
+implementation; and every documented argument error must be reported before
+anything is enqueued.  The error-path tests hand the library fake device
+addresses that validation rejects; they are skipped when a GPU is visible so
+that a validation bug could never turn into a launch on bogus pointers (the
+GPU suite repeats them with real allocations).
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_zero_amd as Z
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zero_shard.h")
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="fake-address error paths run only without a GPU")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names) - {"defined"})
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) >= {"zs_layout", "zs_workspace_bytes", "zs_state_bytes",
+                          "zs_comm_bytes", "shard_grad_sqnorm", "zero_shard_step",
+                          "shard_pack_gather", "zs_strerror"}
+    L = C.CDLL(Z.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in zero_shard.h but not exported"
+
+
+def test_strerror_covers_codes():
+    for code in range(-11, 1):
+        assert Z.zs_strerror(code) != "unknown error"
+    assert Z.zs_strerror(-999) == "unknown error"
+
+
+@pytest.mark.parametrize("align", [1, 8, 128, 2048])
+def test_layout_matches_oracle(align):
+    for psi in list(range(1, 40)) + [1000, 4099, 1 << 20, 218_112_000, 7_000_000_000]:
+        for n_d in (1, 2, 3, 4, 7, 8, 64):
+            for stage in (0, 2, 3):
+                for k in sorted({0, 1 % n_d, n_d // 2, n_d - 1}):
+                    s = Z.zs_layout(psi, n_d, k, align, stage)
+                    assert (s.shard_len, s.shard_offset, s.valid_len) == \
+                        O.layout(psi, n_d, k, align, stage)
+                    assert (s.psi, s.n_d, s.rank, s.align, s.stage) == (psi, n_d, k, align, stage)
+
+
+def test_layout_errors():
+    cases = [((0, 4, 0, 8, 2), Z.ZS_EINVAL_PSI), ((10, 0, 0, 8, 2), Z.ZS_EINVAL_ND),
+             ((10, 4, 4, 8, 2), Z.ZS_EINVAL_RANK), ((10, 4, -1, 8, 2), Z.ZS_EINVAL_RANK),
+             ((10, 4, 0, 0, 2), Z.ZS_EINVAL_LAYOUT), ((10, 4, 0, 8, 4), Z.ZS_EINVAL_STAGE)]
+    for args, code in cases:
+        with pytest.raises(Z.ZSError) as e:
+            Z.zs_layout(*args)
+        assert e.value.code == code
+    with pytest.raises(Z.ZSError) as e:
+        Z.zs_layout(10, 4, 0, 8, 2, out_mode=7)
+    assert e.value.code == Z.ZS_EINVAL_STAGE
+    assert Z.lib().zs_layout(10, 4, 0, 8, 2, 0, None) == Z.ZS_ENULL
+
+
+def test_accounting_matches_oracle():
+    for psi in (1.0, 7e9, 13e9, 70e9, 405e9):
+        for n_d in (1, 4, 8, 32, 64, 128):
+            for stage in range(4):
+                a = Z.zs_state_bytes(psi, n_d, stage)
+                b = O.state_bytes(psi, n_d, stage)
+                assert abs(a - b) <= 1e-15 * b
+                a = Z.zs_comm_bytes(psi, n_d, stage)
+                b = O.comm_bytes(psi, n_d, stage)
+                assert abs(a - b) <= 1e-15 * max(b, 1.0)
+    assert Z.zs_state_bytes(0, 8, 2) == -1 and Z.zs_state_bytes(1e9, 0, 2) == -1
+    assert Z.zs_state_bytes(1e9, 8, 5) == -1 and Z.zs_comm_bytes(1e9, 8, -1) == -1
+
+
+# ---- error paths (validation happens before anything is enqueued) -------------------
+
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+MIS = FAKE + 2                 # misaligned
+
+
+def _step(s, h, slices=None, mean=None, sq=None, w=FAKE, m=FAKE, v=FAKE, out=FAKE):
+    sl = None if slices is None else (C.c_void_p * len(slices))(*slices)
+    return Z.lib().zero_shard_step(C.byref(s), C.byref(h), sl, mean, sq, 0.0, w, m, v, out,
+                                   None)
+
+
+def _sq(s, slices, mean=None, ws=FAKE, wsb=None, out=FAKE):
+    sl = None if slices is None else (C.c_void_p * len(slices))(*slices)
+    if wsb is None:
+        wsb = Z.zs_workspace_bytes(s)
+    return Z.lib().shard_grad_sqnorm(C.byref(s), sl, mean, ws, wsb, out, 0, None)
+
+
+@no_gpu
+def test_step_error_paths():
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    h = Z.adamw(step=1, max_grad_norm=1.0)
+    sl = [FAKE] * 4
+    # shard inconsistent with zs_layout
+    bad = Z.zs_shard.from_buffer_copy(s)
+    bad.valid_len += 1
+    assert _step(bad, h, slices=sl, sq=FAKE) == Z.ZS_EINVAL_LAYOUT
+    bad = Z.zs_shard.from_buffer_copy(s)
+    bad.shard_offset = 0
+    assert _step(bad, h, slices=sl, sq=FAKE) == Z.ZS_EINVAL_LAYOUT
+    bad = Z.zs_shard.from_buffer_copy(s)
+    bad.psi = 0
+    assert _step(bad, h, slices=sl, sq=FAKE) == Z.ZS_EINVAL_PSI
+    # shard_len not a multiple of 8
+    s_odd = Z.zs_layout(1000, 4, 1, 1, 2)
+    assert s_odd.shard_len == 250
+    assert _step(s_odd, h, slices=sl, sq=FAKE) == Z.ZS_EALIGN
+    # too many ranks
+    s65 = Z.zs_layout(65 * 8, 65, 0, 8, 2)
+    assert _step(s65, h, slices=[FAKE] * 65, sq=FAKE) == Z.ZS_EUNSUPPORTED
+    # hyperparameters
+    for kw in (dict(lr=-1.0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0),
+               dict(weight_decay=-0.1), dict(step=0), dict(lr=float("nan")),
+               dict(max_grad_norm=float("inf"))):
+        assert _step(s, Z.adamw(**kw), slices=sl, sq=FAKE) == Z.ZS_EINVAL_HPARAM, kw
+    # both / neither gradient source; clip without the squared norm
+    assert _step(s, h, slices=sl, mean=FAKE, sq=FAKE) == Z.ZS_ENULL
+    assert _step(s, h, sq=FAKE) == Z.ZS_ENULL
+    assert _step(s, h, slices=sl) == Z.ZS_ENULL
+    assert _step(s, h, slices=[FAKE, FAKE, None, FAKE], sq=FAKE) == Z.ZS_ENULL
+    assert _step(s, h, slices=sl, sq=FAKE, w=None) == Z.ZS_ENULL
+    assert _step(s, h, slices=sl, sq=FAKE, out=None) == Z.ZS_ENULL
+    # alignment
+    assert _step(s, h, slices=[FAKE, MIS, FAKE, FAKE], sq=FAKE) == Z.ZS_EALIGN
+    assert _step(s, h, mean=MIS, sq=FAKE) == Z.ZS_EALIGN
+    assert _step(s, h, slices=sl, sq=FAKE + 4) == Z.ZS_EALIGN
+    assert _step(s, h, slices=sl, sq=FAKE, m=MIS) == Z.ZS_EALIGN
+    assert _step(s, h, slices=sl, sq=FAKE, out=MIS) == Z.ZS_EALIGN
+    # invalid stage / out_mode inside the struct
+    bad = Z.zs_shard.from_buffer_copy(s)
+    bad.out_mode = 3
+    assert _step(bad, h, slices=sl, sq=FAKE) == Z.ZS_EINVAL_STAGE
+    assert Z.lib().zero_shard_step(None, C.byref(h), None, FAKE, FAKE, 0.0, FAKE, FAKE, FAKE,
+                                   FAKE, None) == Z.ZS_ENULL
+
+
+@no_gpu
+def test_sqnorm_and_pack_error_paths():
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    sl = [FAKE] * 4
+    assert _sq(s, None) == Z.ZS_ENULL
+    assert _sq(s, sl, ws=None) == Z.ZS_ENULL
+    assert _sq(s, sl, out=None) == Z.ZS_ENULL
+    assert _sq(s, sl, wsb=Z.zs_workspace_bytes(s) - 8) == Z.ZS_EWORKSPACE
+    assert _sq(s, sl, ws=MIS) == Z.ZS_EALIGN
+    assert _sq(s, sl, mean=MIS) == Z.ZS_EALIGN
+    assert _sq(s, [FAKE, FAKE, FAKE, MIS]) == Z.ZS_EALIGN
+    assert _sq(s, [FAKE, None, FAKE, FAKE]) == Z.ZS_ENULL
+    L = Z.lib()
+    assert L.shard_pack_gather(C.byref(s), FAKE, None, None) == Z.ZS_ENULL
+    assert L.shard_pack_gather(C.byref(s), None, FAKE, None) == Z.ZS_ENULL
+    assert L.shard_pack_gather(C.byref(s), MIS, FAKE, None) == Z.ZS_EALIGN
+    assert L.shard_pack_gather(C.byref(s), FAKE, MIS, None) == Z.ZS_EALIGN
+
+
+def test_workspace_is_modest():
+    s = Z.zs_layout(7_000_000_000, 8, 3, 1, 2)
+    assert 0 < Z.zs_workspace_bytes(s) <= 64 * 1024

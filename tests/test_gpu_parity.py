@@ -1,0 +1,570 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every expected value comes from the oracle on inputs drawn by the host side
+of the seeded generator (see parity_util).  The bar: bit-exact for layout,
+pads, untouched gather slots and integer work; fp32 master/m/v within 2e-6
+relative error and bf16 parameters within 1 ulp (bit-exact is expected
+whenever the clip coefficient cannot depend on the fp64 summation order, and
+is asserted then).  Run on an MI355X:  pytest -m gpu -s
+"""
+import ctypes as C
+
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_zero_amd as Z
+import oracle as O
+import zsgen
+from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
+from zsgen.workloads import WORKLOADS, STREAM_MASTER
+from parity_util import (assert_bf16_close, assert_state_close, coef_is_robust,
+                         host_slices_at, log, oracle_full_run,
+                         oracle_sampled_step, oracle_sqnorm_chunked, rel_err,
+                         sample_indices)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC1          # bf16 NaN pattern nothing in the step writes
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def dev16(a: np.ndarray, n=None):
+    """Upload uint16 bit patterns into an int16 device tensor of length n."""
+    n = a.size if n is None else n
+    t = torch.full((max(n, 8),), SENTINEL, dtype=torch.int16)
+    t[:a.size] = torch.from_numpy(a.view(np.int16))
+    return t.cuda()
+
+
+def dev32(a: np.ndarray):
+    t = torch.zeros(max(a.size, 8), dtype=torch.float32)
+    t[:a.size] = torch.from_numpy(a)
+    return t.cuda()
+
+
+def host16(t, n=None):
+    x = t.cpu().numpy().view(np.uint16)
+    return x if n is None else x[:n]
+
+
+def host32(t, n):
+    return t.cpu().numpy()[:n]
+
+
+def run_small_case(psi, n_d, rank, align, stage, out_mode, h, slices, w, m, v,
+                   mode, other_sqnorm=0.0):
+    """One shard step on the GPU from host arrays.  mode: 'slices' (no clip),
+    'mean' (clip, stored mean) or 'reread' (clip, slices read twice)."""
+    s = Z.zs_layout(psi, n_d, rank, align, stage, out_mode)
+    S, V = s.shard_len, s.valid_len
+    out_len = n_d * S if (out_mode == Z.ZS_OUT_GATHER and stage != 0) else S
+    # rows of S elements; the part beyond V holds junk the kernels must not read
+    rows = torch.full((n_d, S), 0x7F80, dtype=torch.int16)          # +Inf junk
+    for r in range(n_d):
+        rows[r, :V] = torch.from_numpy(slices[r][:V].view(np.int16))
+    rows = rows.cuda()
+    ptrs = [rows.data_ptr() + 2 * S * r for r in range(n_d)]
+    dw, dm, dv = dev32(w), dev32(m), dev32(v)
+    out = torch.full((out_len,), SENTINEL, dtype=torch.int16, device="cuda")
+    mean = torch.zeros(max(V, 8), dtype=torch.float32, device="cuda")
+    ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    if mode == "slices":
+        Z.zero_shard_step(s, h, grad_slices=ptrs, master=dw, exp_avg=dm, exp_avg_sq=dv,
+                          param_out=out)
+    elif mode == "mean":
+        Z.shard_grad_sqnorm(s, ptrs, mean, ws, sq)
+        Z.zero_shard_step(s, h, mean_in=mean, sqnorm=sq, other_sqnorm=other_sqnorm, master=dw,
+                          exp_avg=dm, exp_avg_sq=dv, param_out=out)
+    elif mode == "reread":
+        Z.shard_grad_sqnorm(s, ptrs, None, ws, sq)
+        Z.zero_shard_step(s, h, grad_slices=ptrs, sqnorm=sq, other_sqnorm=other_sqnorm,
+                          master=dw, exp_avg=dm, exp_avg_sq=dv, param_out=out)
+    torch.cuda.synchronize()
+    return (s, host32(dw, V), host32(dm, V), host32(dv, V), host16(out),
+            float(sq.item()), host32(mean, V))
+
+
+def zs_h(h: O.Hparams):
+    return Z.adamw(lr=h.lr, beta1=h.beta1, beta2=h.beta2, eps=h.eps,
+                   weight_decay=h.weight_decay, step=h.step, max_grad_norm=h.max_grad_norm)
+
+
+def check_against_oracle(case, s, res, slices, w, m, v, h, other_sqnorm, mode):
+    _, gw, gm, gv, gout, gq, gmean = res
+    S, off, V = s.shard_len, s.shard_offset, s.valid_len
+    ow, om, ov = w[:V].copy(), m[:V].copy(), v[:V].copy()
+    oout, oq, ocoef = O.shard_step(s.n_d, S, V, h, [x[:V].copy() for x in slices], ow, om, ov,
+                                   other_sqnorm=other_sqnorm)
+    base = off if (s.out_mode == Z.ZS_OUT_GATHER and s.stage != 0) else 0
+    slot = gout[base:base + S]
+    outside = np.concatenate([gout[:base], gout[base + S:]])
+    assert np.all(outside == SENTINEL), f"{case}: wrote outside its slot"
+    assert np.all(slot[V:] == 0), f"{case}: pads not zero"
+    if mode != "slices":
+        assert abs(gq - oq) <= 1e-12 * max(abs(oq), 1e-300), f"{case}: sqnorm {gq} vs {oq}"
+    if mode == "mean":
+        assert np.array_equal(gmean.view(np.uint32), O.reduce_mean(
+            [x[:V].copy() for x in slices]).view(np.uint32)), f"{case}: mean differs"
+    bitwise_expected = mode == "slices" or coef_is_robust(oq + other_sqnorm, h.max_grad_norm)
+    for name, a, b in (("w", gw, ow), ("m", gm, om), ("v", gv, ov)):
+        e = rel_err(a, b)
+        assert e.size == 0 or e.max() <= 2e-6, f"{case}: {name} rel err {e.max()}"
+        if bitwise_expected:
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{case}: {name} bits"
+    if bitwise_expected:
+        assert np.array_equal(slot, oout), f"{case}: bf16 out bits"
+
+
+# ---- the generator's two sides agree ---------------------------------------------------
+
+def test_generator_device_matches_host():
+    for start, n in [(0, 1), (1, 1), (7, 1001), (1 << 20, 3 << 20), (874_999_000, 1000),
+                     (2_000_000_001, 4097)]:
+        d32 = torch.empty(n, dtype=torch.float32, device="cuda")
+        zsgen.dev_f32(d32, 2, STREAM_MASTER, 3, 0, 0.02, start)
+        h32 = zsgen.host_f32(2, STREAM_MASTER, 3, 0, 0.02, start, n)
+        assert np.array_equal(d32.cpu().numpy().view(np.uint32), h32.view(np.uint32)), (start, n)
+        d32a = torch.empty(n, dtype=torch.float32, device="cuda")
+        zsgen.dev_f32(d32a, 2, 3, 0, 0, 1e-6, start, absval=True)
+        h32a = zsgen.host_f32(2, 3, 0, 0, 1e-6, start, n, absval=True)
+        assert np.array_equal(d32a.cpu().numpy().view(np.uint32), h32a.view(np.uint32))
+        d16 = torch.empty(n, dtype=torch.int16, device="cuda")
+        zsgen.dev_bf16(d16, 1, 4, 5, 3, 1e-3, start, p_out=0.01, sigma_out=0.1)
+        h16 = zsgen.host_bf16(1, 4, 5, 3, 1e-3, start, n, p_out=0.01, sigma_out=0.1)
+        assert np.array_equal(d16.cpu().numpy().view(np.uint16), h16), (start, n)
+    log("generator: device == host on all ranges")
+
+
+# ---- the pages' worked example ---------------------------------------------------------
+
+def test_worked_example_on_gpu():
+    """Two GPUs with half-batch means -1.5 and -13 (and four ranks with the
+    per-sample gradients) step exactly like one GPU with the mean -7.25."""
+    def bf(vals):
+        return O.bf16_rne(np.array(vals, np.float32))
+    h = O.Hparams(lr=1e-2, weight_decay=0.1, step=3)
+    w, m, v = (np.array([x], np.float32) for x in (1.0, 0.25, 3.0))
+    results = []
+    for grads in ([-1.5, -13.0], [-1.0, -2.0, -6.0, -20.0], [-7.25]):
+        sl = [bf([x]) for x in grads]
+        res = run_small_case(1, len(grads), 0, 8, 0, Z.ZS_OUT_SHARD, zs_h(h), sl, w, m, v,
+                             "slices")
+        s = res[0]
+        check_against_oracle("worked", s, res, sl, w, m, v, h, 0.0, "slices")
+        results.append((res[1].tobytes(), res[2].tobytes(), res[3].tobytes(), res[4][:8].tobytes()))
+    assert results[0] == results[2] and results[1] == results[2]
+
+
+# ---- small and ragged shapes, every mode -----------------------------------------------
+
+@pytest.mark.parametrize("mode", ["slices", "mean", "reread"])
+def test_ragged_shapes(mode):
+    rng = np.random.default_rng({"slices": 1, "mean": 2, "reread": 3}[mode])
+    n_cases = 0
+    for psi in (1, 9, 1000, 4099, 1_000_003):
+        for n_d in (1, 2, 3, 4, 8, 64):
+            for rank in sorted({0, n_d // 2, n_d - 1}):
+                for stage, out_mode in ((2, Z.ZS_OUT_GATHER), (3, Z.ZS_OUT_SHARD)):
+                    s = Z.zs_layout(psi, n_d, rank, 8, stage, out_mode)
+                    V = s.valid_len
+                    sl = [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32))
+                          for _ in range(n_d)]
+                    w = rng.normal(0, 0.02, V).astype(np.float32)
+                    m = rng.normal(0, 1e-4, V).astype(np.float32)
+                    v = np.abs(rng.normal(0, 1e-6, V)).astype(np.float32)
+                    clip = 0.0 if mode == "slices" else 0.05
+                    h = O.Hparams(lr=3e-4, weight_decay=0.1, step=1 + n_cases % 7,
+                                  max_grad_norm=clip)
+                    other = 1e-4 if mode != "slices" else 0.0
+                    res = run_small_case(psi, n_d, rank, 8, stage, out_mode, zs_h(h), sl, w, m,
+                                         v, mode, other_sqnorm=other)
+                    check_against_oracle((psi, n_d, rank, stage, mode), res[0], res, sl, w, m,
+                                         v, h, other, mode)
+                    n_cases += 1
+    log(f"ragged shapes, mode {mode}: {n_cases} cases")
+
+
+def test_stage0_ddp_equals_concatenated_shards():
+    """One DDP step (stage 0: every rank updates the whole vector) equals the
+    concatenation of the N_d ZeRO shard steps, bit for bit, on the GPU."""
+    rng = np.random.default_rng(21)
+    psi, n_d = 100_003, 4
+    full = [O.bf16_rne(rng.normal(0, 1e-3, psi).astype(np.float32)) for _ in range(n_d)]
+    w = rng.normal(0, 0.02, psi).astype(np.float32)
+    m = rng.normal(0, 1e-4, psi).astype(np.float32)
+    v = np.abs(rng.normal(0, 1e-6, psi)).astype(np.float32)
+    h = zs_h(O.Hparams(step=5))
+    ddp = run_small_case(psi, n_d, 0, 8, 0, Z.ZS_OUT_GATHER, h, full, w, m, v, "slices")
+    cat_w = np.empty(psi, np.float32)
+    cat_out = np.empty(psi, np.uint16)
+    for k in range(n_d):
+        s = Z.zs_layout(psi, n_d, k, 8, 1)
+        off, V = s.shard_offset, s.valid_len
+        part = run_small_case(psi, n_d, k, 8, 1, Z.ZS_OUT_GATHER, h,
+                              [x[off:off + V].copy() for x in full], w[off:off + V].copy(),
+                              m[off:off + V].copy(), v[off:off + V].copy(), "slices")
+        cat_w[off:off + V] = part[1]
+        cat_out[off:off + V] = part[4][off:off + V]
+    assert np.array_equal(cat_w.view(np.uint32), ddp[1].view(np.uint32))
+    assert np.array_equal(cat_out, ddp[4][:psi])
+
+
+# ---- workloads -------------------------------------------------------------------------
+
+def _compare_full(name, run, unit_data, wl, rank, steps):
+    s = run.shard
+    ow, om, ov, oout, qs, coefs = oracle_full_run(wl, rank, steps, wl.t0, s)
+    V, S, off = s.valid_len, s.shard_len, s.shard_offset
+    gw, gm, gv = (host32(x, V) for x in (unit_data.w, unit_data.m, unit_data.v))
+    gout = host16(unit_data.out)
+    base = off if wl.out_mode == "gather" else 0
+    slot = gout[base:base + S]
+    assert np.all(np.delete(gout, np.arange(base, base + S)) == SENTINEL)
+    assert np.all(slot[V:] == 0)
+    nb = 0
+    nb += assert_state_close(f"{name} w", gw, ow)
+    nb += assert_state_close(f"{name} m", gm, om)
+    nb += assert_state_close(f"{name} v", gv, ov)
+    nb += assert_bf16_close(f"{name} out", slot[:V], oout[:V])
+    return nb, qs, coefs
+
+
+def test_tiny_workload_ten_steps():
+    wl = WORKLOADS["tiny"]
+    run = ShardRun(wl)
+    run.fill_state(out_fill=SENTINEL)
+    for i in range(wl.steps):
+        run.fill_grads(wl.t0 + i)
+        run.step(wl.t0 + i)
+    torch.cuda.synchronize()
+    nb, _, _ = _compare_full("tiny", run, run.units_data[0], wl, wl.rank, wl.steps)
+    assert nb == 0, "no clip: the HIP path must match the oracle bit for bit"
+
+
+@pytest.mark.parametrize("rank", [3, 7])
+def test_gpt2_small_workload_five_steps(rank):
+    wl = WORKLOADS["gpt2_small"]
+    run = ShardRun(wl, rank=rank)
+    run.fill_state(out_fill=SENTINEL)
+    gq = []
+    for i in range(wl.steps):
+        run.fill_grads(wl.t0 + i)
+        run.step(wl.t0 + i)
+        gq.append(float(run.sqnorm.item()))
+    torch.cuda.synchronize()
+    nb, qs, coefs = _compare_full(f"gpt2_small rank {rank}", run, run.units_data[0], wl, rank,
+                                  wl.steps)
+    for a, b in zip(gq, qs):
+        assert abs(a - b) <= 1e-12 * b
+    assert all(c < 1 for c in coefs), "the clip is active in this workload"
+    if all(coef_is_robust(q, wl.max_grad_norm) for q in qs):
+        assert nb == 0
+
+
+def _sampled_check(name, wl, run, unit, t, idx, coef):
+    s = run.shard
+    d = run.units_data[unit]
+    ow, om, ov, oout, og = oracle_sampled_step(wl, unit, t, s, idx, coef)
+    ti = torch.from_numpy(idx).cuda()
+    base = s.shard_offset if wl.out_mode == "gather" else 0
+    gw = d.w[ti].cpu().numpy()
+    gm = d.m[ti].cpu().numpy()
+    gv = d.v[ti].cpu().numpy()
+    gout = d.out[ti + base].cpu().numpy().view(np.uint16)
+    nb = assert_state_close(f"{name} w", gw, ow)
+    nb += assert_state_close(f"{name} m", gm, om)
+    nb += assert_state_close(f"{name} v", gv, ov)
+    nb += assert_bf16_close(f"{name} out", gout, oout)
+    if d.mean is not None:
+        gmean = d.mean[ti].cpu().numpy()
+        assert np.array_equal(gmean.view(np.uint32), og.view(np.uint32)), f"{name}: mean bits"
+    return nb
+
+
+def _check_slot_edges(wl, run, unit):
+    """Pads are zero; the slots of the other ranks still hold the sentinel."""
+    s = run.shard
+    d = run.units_data[unit]
+    S, V = s.shard_len, s.valid_len
+    base = s.shard_offset if wl.out_mode == "gather" else 0
+    assert bool((d.out[base + V:base + S] == 0).all())
+    if wl.out_mode == "gather":
+        assert bool((d.out[:base] == SENTINEL).all())
+        assert bool((d.out[base + S:] == SENTINEL).all())
+
+
+def test_zero2_7b_full_size():
+    wl = WORKLOADS["zero2_7b"]
+    log("zero2_7b: allocating ~42 GB and filling on the device")
+    run = ShardRun(wl)
+    run.fill_state(out_fill=SENTINEL)
+    run.fill_grads(wl.t0)
+    run.step(wl.t0)
+    torch.cuda.synchronize()
+    gq = float(run.sqnorm.item())
+    V = run.V
+    idx = sample_indices(V, 1 << 20, seed=2)
+    log(f"zero2_7b: GPU done (Q={gq:.6g}); oracle squared norm over {V:,} params")
+    oq = oracle_sqnorm_chunked(wl, 0, wl.t0, run.shard.shard_offset, V)
+    log(f"zero2_7b: oracle Q={oq:.17g} GPU Q={gq:.17g}")
+    assert abs(gq - oq) <= 1e-12 * oq
+    coef = O.clip_coef(oq, wl.max_grad_norm)
+    assert coef < 1
+    nb = _sampled_check("zero2_7b", wl, run, 0, wl.t0, idx, coef)
+    _check_slot_edges(wl, run, 0)
+    if coef_is_robust(oq, wl.max_grad_norm):
+        assert nb == 0
+
+
+def test_fsdp_llama_units_full_size():
+    wl = WORKLOADS["fsdp_llama_units"]
+    log("fsdp_llama_units: allocating 32 units (~42 GB)")
+    run = ShardRun(wl)
+    run.fill_state(out_fill=SENTINEL)
+    run.fill_grads(wl.t0)
+    run.step(wl.t0)
+    torch.cuda.synchronize()
+    gq = float(run.sqnorm.item())
+    s = run.shard
+    assert s.valid_len == 27_256_832 and s.shard_len == 27_265_024
+    log("fsdp_llama_units: oracle squared norm over 32 units")
+    oq = 0.0
+    for u in range(wl.units):
+        oq += oracle_sqnorm_chunked(wl, u, wl.t0, s.shard_offset, s.valid_len)
+    log(f"fsdp_llama_units: oracle Q={oq:.17g} GPU Q={gq:.17g}")
+    assert abs(gq - oq) <= 1e-12 * oq
+    coef = O.clip_coef(oq, wl.max_grad_norm)
+    nb = 0
+    for u in (0, 1, 17, 31):
+        idx = sample_indices(s.valid_len, 1 << 17, seed=100 + u)
+        nb += _sampled_check(f"fsdp unit {u}", wl, run, u, wl.t0, idx, coef)
+        _check_slot_edges(wl, run, u)
+    if coef_is_robust(oq, wl.max_grad_norm):
+        assert nb == 0
+
+
+def test_zero3_70b_full_size():
+    """64 gradient slices, 1.09e9 parameters (~160 GB in HBM).  The oracle
+    cannot regenerate 70e9 gradients in a test's time, so: (1) the stored mean
+    is compared bit for bit at sampled positions; (2) the squared norm is
+    checked exactly by the oracle on two sub-ranges and for additivity over
+    eight sub-ranges; (3) the fused step is compared at sampled positions with
+    the clip taken out (max_grad_norm 0), where no global sum is involved."""
+    import dataclasses
+    wl = WORKLOADS["zero3_70b"]
+    log("zero3_70b: allocating ~160 GB and filling on the device")
+    run = ShardRun(wl)
+    run.fill_state()
+    run.fill_grads(wl.t0)
+    run.reduce_pass()
+    torch.cuda.synchronize()
+    gq = float(run.sqnorm.item())
+    s, d = run.shard, run.units_data[0]
+    V = s.valid_len
+    idx = sample_indices(V, 1 << 18, seed=4)
+    og = O.reduce_mean(host_slices_at(wl, 0, wl.t0, s.shard_offset + idx))
+    gmean = d.mean[torch.from_numpy(idx).cuda()].cpu().numpy()
+    assert np.array_equal(gmean.view(np.uint32), og.view(np.uint32))
+    log("zero3_70b: sampled 64-rank mean is bit-exact")
+    # additivity of the squared norm over 8 sub-ranges, two checked by the oracle
+    parts = []
+    L = (V // 8) // 8 * 8            # sub-range lengths stay multiples of 8
+    ws = run.workspace
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for j in range(8):
+        a = j * L
+        n = L if j < 7 else V - a
+        sub = Z.zs_layout(64 * n, 64, 0, 1, 3, Z.ZS_OUT_SHARD)
+        assert sub.valid_len == n and n % 8 == 0
+        ptrs = [p + 2 * a for p in run.slice_ptrs(d)]
+        Z.shard_grad_sqnorm(sub, ptrs, None, ws, sq)
+        parts.append(float(sq.item()))
+    assert abs(sum(parts) - gq) <= 1e-12 * gq
+    for j in (0, 7):
+        a = j * L
+        n = min(1 << 22, L)
+        sub = Z.zs_layout(64 * n, 64, 0, 1, 3, Z.ZS_OUT_SHARD)
+        ptrs = [p + 2 * a for p in run.slice_ptrs(d)]
+        Z.shard_grad_sqnorm(sub, ptrs, None, ws, sq)
+        g_sub = float(sq.item())
+        o_sub = oracle_sqnorm_chunked(wl, 0, wl.t0, s.shard_offset + a, n)
+        assert abs(g_sub - o_sub) <= 1e-12 * o_sub, (j, g_sub, o_sub)
+    log(f"zero3_70b: Q={gq:.6g}; sub-range sums and oracle sub-ranges agree")
+    # the fused 64-slice step without the clip, at full size
+    wl_nc = dataclasses.replace(wl, max_grad_norm=0.0)
+    h_nc = Z.adamw(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                   weight_decay=wl.weight_decay, step=wl.t0, max_grad_norm=0.0)
+    Z.zero_shard_step(s, h_nc, grad_slices=run.slice_ptrs(d), master=d.w, exp_avg=d.m,
+                      exp_avg_sq=d.v, param_out=d.out)
+    torch.cuda.synchronize()
+    nb = _sampled_check("zero3_70b (no clip)", wl_nc, run, 0, wl.t0, idx, None)
+    assert nb == 0
+    assert bool((d.out[V:] == 0).all())
+
+
+# ---- properties ---------------------------------------------------------------------------
+
+def test_run_to_run_bitwise_deterministic():
+    wl = WORKLOADS["gpt2_small"]
+    outs = []
+    for _ in range(2):
+        run = ShardRun(wl)
+        run.fill_state(out_fill=SENTINEL)
+        run.fill_grads(1)
+        run.step(1)
+        torch.cuda.synchronize()
+        d = run.units_data[0]
+        outs.append((run.sqnorm.cpu().numpy().tobytes(), d.w.cpu().numpy().tobytes(),
+                     d.m.cpu().numpy().tobytes(), d.v.cpu().numpy().tobytes(),
+                     d.out.cpu().numpy().tobytes()))
+        del run
+    assert outs[0] == outs[1]
+
+
+def test_reread_schedule_matches_materialised_mean():
+    """Clip with the slices read again in the step gives the same bits as the
+    stored-mean schedule."""
+    wl = WORKLOADS["gpt2_small"]
+    res = []
+    for store in (True, False):
+        run = ShardRun(wl, store_mean=store)
+        run.fill_state(out_fill=SENTINEL)
+        run.fill_grads(2)
+        run.step(2)
+        torch.cuda.synchronize()
+        d = run.units_data[0]
+        res.append((d.w.cpu().numpy()[:run.V].tobytes(), d.out.cpu().numpy().tobytes()))
+        del run
+    assert res[0] == res[1]
+
+
+def test_two_steps_equal_step_roundtrip_step():
+    """Checkpoint/resume: the library is stateless, so stepping, copying the
+    shard state to the host and back, and stepping again gives the same bits."""
+    wl = WORKLOADS["tiny"]
+    a = ShardRun(wl)
+    a.fill_state()
+    b = ShardRun(wl)
+    b.fill_state()
+    for t in (1, 2):
+        a.fill_grads(t)
+        a.step(t)
+    b.fill_grads(1)
+    b.step(1)
+    torch.cuda.synchronize()
+    db = b.units_data[0]
+    saved = [x.cpu() for x in (db.w, db.m, db.v)]
+    for x in (db.w, db.m, db.v):
+        x.fill_(float("nan"))
+    for x, y in zip((db.w, db.m, db.v), saved):
+        x.copy_(y.cuda())
+    b.fill_grads(2)
+    b.step(2)
+    torch.cuda.synchronize()
+    da = a.units_data[0]
+    for x, y in zip((da.w, da.m, da.v, da.out), (db.w, db.m, db.v, db.out)):
+        assert torch.equal(x.view(torch.int32) if x.dtype == torch.float32 else x,
+                           y.view(torch.int32) if y.dtype == torch.float32 else y)
+
+
+def test_nan_and_inf_propagate_like_the_oracle():
+    rng = np.random.default_rng(5)
+    psi, n_d = 4099, 4
+    sl = [O.bf16_rne(rng.normal(0, 1e-3, psi).astype(np.float32)) for _ in range(n_d)]
+    sl[2][17] = 0x7FC0                 # NaN in rank 2
+    sl[1][100] = 0x7F80                # +Inf in rank 1
+    sl[3][100] = 0xFF80                # -Inf in rank 3 -> NaN mean
+    sl[0][200] = 0x7F80                # +Inf alone
+    w = rng.normal(0, 0.02, psi).astype(np.float32)
+    m = np.zeros(psi, np.float32)
+    v = np.zeros(psi, np.float32)
+    for mode, clip in (("slices", 0.0), ("mean", 1.0)):
+        h = O.Hparams(step=2, max_grad_norm=clip)
+        res = run_small_case(psi, n_d, 0, 8, 0, Z.ZS_OUT_SHARD, zs_h(h), sl, w, m, v, mode)
+        s = res[0]
+        ow, om, ov = w.copy(), m.copy(), v.copy()
+        oout, oq, _ = O.shard_step(n_d, s.shard_len, psi, h, sl, ow, om, ov)
+        for a, b in ((res[1], ow), (res[2], om), (res[3], ov)):
+            assert np.array_equal(np.isnan(a), np.isnan(b))
+            fin = ~np.isnan(b)
+            assert np.array_equal(a[fin].view(np.uint32), b[fin].view(np.uint32))
+        assert np.array_equal(res[4][:psi], oout[:psi])
+        if clip:
+            assert np.isnan(res[5]) and np.isnan(oq)
+            assert np.isnan(res[1]).all()      # a NaN norm poisons the whole step
+
+
+def test_pack_all_fp32_bit_patterns():
+    """shard_pack_gather on every one of the 2^32 fp32 bit patterns equals the
+    oracle's bf16 rounding, NaNs included."""
+    n = 1 << 28
+    s = Z.zs_layout(n, 1, 0, 8, 0, Z.ZS_OUT_SHARD)
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    for c in range(16):
+        start = c * n
+        bits = torch.arange(start, start + n, dtype=torch.int64, device="cuda").to(torch.int32)
+        Z.shard_pack_gather(s, bits.view(torch.float32), out)
+        got = out.cpu().numpy().view(np.uint16)
+        del bits
+        ref = O.bf16_rne(np.arange(start, start + n, dtype=np.uint64).astype(np.uint32)
+                         .view(np.float32))
+        assert np.array_equal(got, ref), f"chunk {c}"
+    log("pack: all 2^32 patterns match")
+
+
+def test_sqnorm_accumulates_in_call_order():
+    rng = np.random.default_rng(9)
+    n_d, psi = 8, 80_000
+    s = Z.zs_layout(psi, n_d, 2, 8, 3, Z.ZS_OUT_SHARD)
+    V = s.valid_len
+    ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    vals = []
+    for u in range(3):
+        sl = [O.bf16_rne(rng.normal(0, 1e-3 * (u + 1), V).astype(np.float32))
+              for _ in range(n_d)]
+        rows = torch.stack([torch.from_numpy(x.view(np.int16)) for x in sl]).cuda()
+        ptrs = [rows.data_ptr() + 2 * V * r for r in range(n_d)]
+        Z.shard_grad_sqnorm(s, ptrs, None, ws, sq, accumulate=u > 0)
+        torch.cuda.synchronize()
+        vals.append((float(sq.item()), O.sqnorm_accum(0.0, O.reduce_mean(sl))))
+        del rows
+    acc = 0.0
+    for g, o in vals:
+        acc += o
+        assert abs(g - acc) <= 1e-12 * acc
+
+
+def test_gpu_error_paths_write_nothing():
+    """Rejected calls with real buffers return the code and leave them alone."""
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    S, V = s.shard_len, s.valid_len
+    rows = torch.zeros((4, S), dtype=torch.int16, device="cuda")
+    ptrs = [rows.data_ptr() + 2 * S * r for r in range(4)]
+    w = torch.ones(V, device="cuda")
+    m = torch.ones(V, device="cuda")
+    v = torch.ones(V, device="cuda")
+    out = torch.full((4 * S,), SENTINEL, dtype=torch.int16, device="cuda")
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    bad = Z.zs_shard.from_buffer_copy(s)
+    bad.valid_len -= 1
+    for shard, h, kw, code in [
+            (bad, Z.adamw(step=1), dict(grad_slices=ptrs), Z.ZS_EINVAL_LAYOUT),
+            (s, Z.adamw(step=0), dict(grad_slices=ptrs), Z.ZS_EINVAL_HPARAM),
+            (s, Z.adamw(step=1, max_grad_norm=1.0), dict(grad_slices=ptrs), Z.ZS_ENULL),
+            (s, Z.adamw(step=1), dict(grad_slices=ptrs[:3] + [ptrs[3] + 2]), Z.ZS_EALIGN)]:
+        with pytest.raises(Z.ZSError) as e:
+            Z.zero_shard_step(shard, h, master=w, exp_avg=m, exp_avg_sq=v, param_out=out,
+                              sqnorm=None, **kw)
+        assert e.value.code == code
+    torch.cuda.synchronize()
+    assert bool((w == 1).all() and (m == 1).all() and (v == 1).all())
+    assert bool((out == SENTINEL).all())
