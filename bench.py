@@ -61,7 +61,8 @@ def cpu_baseline(wl, shard, seconds: float):
     h = O.Hparams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
                   weight_decay=wl.weight_decay, step=wl.t0, max_grad_norm=wl.max_grad_norm)
     chunk = 1 << 22
-    done, spent, q = 0, 0.0, 0.0
+    done, spent = 0, 0.0
+    acc = O.SqAcc()
     off, V = shard.shard_offset, shard.valid_len
     while spent < seconds and done < V:
         n = min(chunk, V - done)
@@ -76,15 +77,15 @@ def cpu_baseline(wl, shard, seconds: float):
                             absval=True))
         t0 = time.perf_counter()
         g = O.reduce_mean(sl)
-        q = O.sqnorm_accum(q, g)
-        coef = O.clip_coef(q, wl.max_grad_norm) if wl.max_grad_norm > 0 else None
+        acc.add(g)
+        coef = O.clip_coef(acc.value(), wl.max_grad_norm) if wl.max_grad_norm > 0 else None
         O.adamw_f32(h, g, w, m, v, coef=coef)
         O.pack(n, w)
         spent += time.perf_counter() - t0
         done += n
     return {"value": done / spent / 1e9, "unit": "G params/s", "cores": 1, "kind": "oracle",
             "sample": (f"oracle O1-O5 (rank-order mean of {wl.n_d} bf16 slices, fp64 "
-                       f"squared norm, clip, fp32 AdamW, bf16 pack) on the first {done:,} "
+                       f"exact squared norm, clip, fp32 AdamW, bf16 pack) on the first {done:,} "
                        f"of the {V:,} shard parameters of workload {wl.name}, single "
                        f"thread, {spent:.1f} s of oracle time; input generation untimed"),
             "seconds": spent}

@@ -102,8 +102,16 @@ def lib():
         L.or_bf16_rne_array.restype = None
         L.or_reduce_mean.argtypes = [i32, C.c_void_p, i64, C.c_void_p]
         L.or_reduce_mean.restype = None
-        L.or_sqnorm_accum.argtypes = [f64, C.c_void_p, i64]
-        L.or_sqnorm_accum.restype = f64
+        L.or_sqacc_size.argtypes = []
+        L.or_sqacc_size.restype = i64
+        L.or_sqacc_init.argtypes = [C.c_void_p]
+        L.or_sqacc_init.restype = None
+        L.or_sqacc_add.argtypes = [C.c_void_p, C.c_void_p, i64]
+        L.or_sqacc_add.restype = None
+        L.or_sqacc_value.argtypes = [C.c_void_p]
+        L.or_sqacc_value.restype = f64
+        L.or_sqnorm.argtypes = [C.c_void_p, i64]
+        L.or_sqnorm.restype = f64
         L.or_clip_coef.argtypes = [f64, f64]
         L.or_clip_coef.restype = f32
         L.or_make_consts.argtypes = [P(_Hparams), P(_Consts)]
@@ -204,8 +212,26 @@ def reduce_mean(slices) -> np.ndarray:
     return out
 
 
-def sqnorm_accum(q: float, g: np.ndarray) -> float:
-    return lib().or_sqnorm_accum(float(q), _ptr(g, np.float32), g.size)
+def sqnorm(g: np.ndarray) -> float:
+    """Exactly rounded sum of g_i^2 (fp32 g)."""
+    return lib().or_sqnorm(_ptr(g, np.float32) if g.size else None, g.size)
+
+
+class SqAcc:
+    """Exact squared-norm accumulator: add chunks in any order, read the
+    exactly rounded total (the sum is exact until value())."""
+
+    def __init__(self):
+        self._buf = C.create_string_buffer(lib().or_sqacc_size())
+        lib().or_sqacc_init(self._buf)
+
+    def add(self, g: np.ndarray) -> "SqAcc":
+        if g.size:
+            lib().or_sqacc_add(self._buf, _ptr(g, np.float32), g.size)
+        return self
+
+    def value(self) -> float:
+        return lib().or_sqacc_value(self._buf)
 
 
 def clip_coef(Q: float, max_norm: float) -> np.float32:

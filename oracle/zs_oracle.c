@@ -147,13 +147,94 @@ void or_reduce_mean(int32_t n_d, const uint16_t* const* slices, int64_t n,
 
 /* ---- O2 / O3 -------------------------------------------------------------- */
 
-double or_sqnorm_accum(double q, const float* g, int64_t n)
+void or_sqacc_init(or_sqacc* a)
+{
+    memset(a, 0, sizeof(*a));
+}
+
+int64_t or_sqacc_size(void) { return (int64_t)sizeof(or_sqacc); }
+
+void or_sqacc_add(or_sqacc* a, const float* g, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) {
-        double x = (double)g[i];
-        q = q + x * x;
+        uint32_t u = f32_bits(g[i]);
+        uint32_t e = (u >> 23) & 0xFFu;
+        uint32_t frac = u & 0x7FFFFFu;
+        if (e == 0xFFu) {                       /* Inf or NaN */
+            if (frac) a->has_nan = 1; else a->has_inf = 1;
+            continue;
+        }
+        /* |g| = M * 2^(max(e,1) - 150), M < 2^24; g^2 = M^2 * 2^(2(max(e,1) - 150)) */
+        uint64_t M = (e == 0) ? frac : (frac | 0x800000u);
+        uint64_t sq = M * M;                     /* < 2^48, exact */
+        uint32_t b = (e == 0) ? 1u : e;
+        uint64_t before = a->lo[b];
+        a->lo[b] = before + sq;
+        if (a->lo[b] < before) a->hi[b] += 1u;  /* carry */
     }
-    return q;
+}
+
+/* Big integer of 32-bit limbs, in units of 2^-298 (the weight of bucket 1). */
+#define OR_LIMBS 24
+
+static void big_add_shifted(uint32_t* L, uint64_t lo, uint64_t hi, int shift)
+{
+    /* add (hi:lo) * 2^shift into L, one bit at a time (slow, plain) */
+    for (int bit = 0; bit < 128; ++bit) {
+        uint64_t word = bit < 64 ? lo : hi;
+        if (!((word >> (bit & 63)) & 1u)) continue;
+        int pos = shift + bit;
+        int limb = pos / 32, off = pos % 32;
+        uint64_t carry = (uint64_t)1 << off;
+        while (carry && limb < OR_LIMBS) {
+            uint64_t s = (uint64_t)L[limb] + carry;
+            L[limb] = (uint32_t)s;
+            carry = s >> 32;
+            ++limb;
+        }
+    }
+}
+
+static int big_bit(const uint32_t* L, int i)
+{
+    return (int)((L[i / 32] >> (i % 32)) & 1u);
+}
+
+double or_sqacc_value(const or_sqacc* a)
+{
+    if (a->has_nan) return NAN;
+    if (a->has_inf) return INFINITY;
+    uint32_t L[OR_LIMBS];
+    memset(L, 0, sizeof(L));
+    for (int b = 1; b < 255; ++b)
+        if (a->lo[b] || a->hi[b]) big_add_shifted(L, a->lo[b], a->hi[b], 2 * (b - 1));
+    int top = -1;
+    for (int i = OR_LIMBS * 32 - 1; i >= 0; --i)
+        if (big_bit(L, i)) { top = i; break; }
+    if (top < 0) return 0.0;
+    if (top < 53) {                             /* fits 53 bits: exact */
+        uint64_t v = 0;
+        for (int i = top; i >= 0; --i) v = (v << 1) | (uint64_t)big_bit(L, i);
+        return ldexp((double)v, -298);
+    }
+    uint64_t mant = 0;                          /* bits top .. top-52 */
+    for (int i = top; i >= top - 52; --i) mant = (mant << 1) | (uint64_t)big_bit(L, i);
+    int round = big_bit(L, top - 53);
+    int sticky = 0;
+    for (int i = top - 54; i >= 0 && !sticky; --i) sticky = big_bit(L, i);
+    if (round && (sticky || (mant & 1u))) {
+        mant += 1;
+        if (mant == ((uint64_t)1 << 53)) { mant >>= 1; top += 1; }
+    }
+    return ldexp((double)mant, top - 52 - 298);
+}
+
+double or_sqnorm(const float* g, int64_t n)
+{
+    or_sqacc a;
+    or_sqacc_init(&a);
+    or_sqacc_add(&a, g, n);
+    return or_sqacc_value(&a);
 }
 
 float or_clip_coef(double Q, double max_norm)
@@ -219,7 +300,7 @@ int or_shard_step(int32_t n_d, int64_t shard_len, int64_t valid_len,
         or_reduce_mean(n_d, slices, valid_len, g);
     }
     int clip = h->max_grad_norm > 0.0;
-    double q = or_sqnorm_accum(0.0, g, valid_len);
+    double q = or_sqnorm(g, valid_len);
     float coef = 1.0f;
     if (clip) coef = or_clip_coef(q + other_sqnorm, h->max_grad_norm);
     or_consts c;

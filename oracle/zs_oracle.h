@@ -101,9 +101,21 @@ void or_reduce_mean(int32_t n_d, const uint16_t* const* slices, int64_t n,
 /* [DPZ] §7 "Common mistakes", last item: with sharded gradients the global
  * norm is an all-reduce of the squared shard norms.  [DDB] reference DDP
  * program: clip_grad_norm_(..., 1.) at the update boundary.
- * or_sqnorm_accum: q + sum over i ascending of (double)g_i * (double)g_i,
- * one double rounding per addition (the products are exact). */
-double or_sqnorm_accum(double q, const float* g, int64_t n);
+ * The squared norm is the plain definition: the exact sum of g_i^2 over the
+ * elements, rounded once to double (round to nearest even).  Each g_i^2 of an
+ * fp32 g_i is an integer below 2^48 times a power of two, so the accumulator
+ * keeps one 128-bit integer sum per exponent; nothing is rounded until
+ * or_sqacc_value.  Any NaN makes the value NaN, else any Inf makes it +Inf. */
+typedef struct {
+    uint64_t lo[255], hi[255];   /* bucket e: sum of squared significands of
+                                    elements with biased exponent e */
+    int32_t has_nan, has_inf;
+} or_sqacc;
+void   or_sqacc_init(or_sqacc* a);
+void   or_sqacc_add(or_sqacc* a, const float* g, int64_t n);
+double or_sqacc_value(const or_sqacc* a);
+int64_t or_sqacc_size(void);
+double or_sqnorm(const float* g, int64_t n);   /* init + add + value */
 /* coef = f32(min(1, max_norm / (sqrt(Q) + 1e-6))) in double; a NaN quotient
  * stays NaN (the clamp propagates it), Q = +Inf gives 0.  The 1e-6 is the
  * library call's constant, not printed on the pages. */
@@ -145,7 +157,7 @@ void or_pack(int64_t shard_len, int64_t valid_len, const float* w,
              uint16_t* out);
 
 /* ---- one whole shard step (O1..O5) ---------------------------------------- */
-/* Applies O1; if h->max_grad_norm > 0, O2 over the shard, Q = local +
+/* Applies O1; if h->max_grad_norm > 0, O2 over the shard (exact), Q = local +
  * other_sqnorm (stand-in for the scalar all-reduce), O3 coef; O4 on the
  * valid_len elements; O5 into out[0 .. shard_len).  Writes the local
  * sqnorm and coef if the pointers are non-NULL (NaN coef reported as 1 when

@@ -86,13 +86,15 @@ def oracle_full_run(wl: Workload, rank: int, steps: int, t0: int, shard, other_s
 
 
 def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
-                          chunk: int = 1 << 24, keep_idx=None):
-    """Oracle squared norm of the mean over [start, start+n), ascending, in
-    chunks (the accumulator is carried, so the order is the plain one).  The
-    host generator fills chunk k+1 while the oracle reduces chunk k.  If
-    keep_idx (sorted, relative to start) is given, also returns the oracle's
-    mean at those positions."""
-    q = 0.0
+                          chunk: int = 1 << 24, keep_idx=None, acc=None):
+    """Oracle squared norm of the mean over [start, start+n): the exact sum,
+    accumulated chunk by chunk and rounded once.  The host generator fills
+    chunk k+1 while the oracle reduces chunk k.  If keep_idx (sorted, relative
+    to start) is given, also returns the oracle's mean at those positions.
+    Pass `acc` to keep accumulating into an existing exact accumulator (the
+    global norm over several FSDP units)."""
+    own = acc is None
+    acc = O.SqAcc() if own else acc
     kept = np.empty(0 if keep_idx is None else len(keep_idx), np.float32)
     starts = list(range(0, n, chunk))
 
@@ -106,12 +108,13 @@ def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
             if ci + 1 < len(starts):
                 fut = ex.submit(gen, starts[ci + 1])
             g = O.reduce_mean(sl)
-            q = O.sqnorm_accum(q, g)
+            acc.add(g)
             if keep_idx is not None:
                 lo, hi = np.searchsorted(keep_idx, [a, a + len(g)])
                 kept[lo:hi] = g[keep_idx[lo:hi] - a]
             if ci % 8 == 7:
                 log(f"  oracle sqnorm {wl.name} unit {unit}: {a + len(g):,}/{n:,}")
+    q = acc.value()
     if keep_idx is not None:
         return q, kept
     return q
@@ -179,12 +182,15 @@ def assert_bf16_close(name, got, ref):
     return nbit
 
 
+Q_REL_BAR = 1e-12       # GPU fp64 tree sum vs the oracle's exactly rounded sum
+
+
 def coef_is_robust(Q: float, max_norm: float) -> bool:
-    """True if every Q' within 1e-12 relative of Q gives the same fp32 clip
-    coefficient (so the GPU's differently ordered fp64 sum cannot change it)."""
+    """True if every Q' within Q_REL_BAR of Q gives the same fp32 clip
+    coefficient (so the GPU's differently rounded fp64 sum cannot change it)."""
     c = O.clip_coef(Q, max_norm)
-    return (O.clip_coef(Q * (1 - 1e-12), max_norm) == c and
-            O.clip_coef(Q * (1 + 1e-12), max_norm) == c)
+    return (O.clip_coef(Q * (1 - Q_REL_BAR), max_norm) == c and
+            O.clip_coef(Q * (1 + Q_REL_BAR), max_norm) == c)
 
 
 def gpu_threads_note():

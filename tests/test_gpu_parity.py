@@ -336,9 +336,10 @@ def test_fsdp_llama_units_full_size():
     s = run.shard
     assert s.valid_len == 27_256_832 and s.shard_len == 27_265_024
     log("fsdp_llama_units: oracle squared norm over 32 units")
-    oq = 0.0
+    acc = O.SqAcc()
     for u in range(wl.units):
-        oq += oracle_sqnorm_chunked(wl, u, wl.t0, s.shard_offset, s.valid_len)
+        oracle_sqnorm_chunked(wl, u, wl.t0, s.shard_offset, s.valid_len, acc=acc)
+    oq = acc.value()
     log(f"fsdp_llama_units: oracle Q={oq:.17g} GPU Q={gq:.17g}")
     assert abs(gq - oq) <= 1e-12 * oq
     coef = O.clip_coef(oq, wl.max_grad_norm)
@@ -535,7 +536,7 @@ def test_sqnorm_accumulates_in_call_order():
         ptrs = [rows.data_ptr() + 2 * V * r for r in range(n_d)]
         Z.shard_grad_sqnorm(s, ptrs, None, ws, sq, accumulate=u > 0)
         torch.cuda.synchronize()
-        vals.append((float(sq.item()), O.sqnorm_accum(0.0, O.reduce_mean(sl))))
+        vals.append((float(sq.item()), O.sqnorm(O.reduce_mean(sl))))
         del rows
     acc = 0.0
     for g, o in vals:

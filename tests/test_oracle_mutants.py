@@ -33,7 +33,13 @@ MUTANTS = {
                             "float s = or_bf16_to_f32(slices[n_d - 1][i]);"),
                            ("s = s + or_bf16_to_f32(slices[r][i]);",
                             "s = s + or_bf16_to_f32(slices[n_d - 1 - r][i]);")],
-    "sqnorm_not_squared": [("q = q + x * x;", "q = q + x;")],
+    "sqnorm_not_squared": [("uint64_t sq = M * M;", "uint64_t sq = M;")],
+    "sqnorm_wrong_weight": [("big_add_shifted(L, a->lo[b], a->hi[b], 2 * (b - 1));",
+                             "big_add_shifted(L, a->lo[b], a->hi[b], 2 * b);")],
+    "sqnorm_drops_subnormals": [("uint32_t b = (e == 0) ? 1u : e;", "uint32_t b = e;")],
+    "sqnorm_truncates": [("if (round && (sticky || (mant & 1u))) {", "if (0) {")],
+    "sqnorm_ties_away": [("if (round && (sticky || (mant & 1u))) {", "if (round) {")],
+    "sqnorm_drops_carry": [("if (a->lo[b] < before) a->hi[b] += 1u;", "(void)before;")],
     "clip_eps_misplaced": [("max_norm / (sqrt(Q) + 1e-6)", "max_norm / sqrt(Q) + 1e-6")],
     "clip_clamp_inverted": [("if (c > 1.0) c = 1.0;", "if (c < 1.0) c = 1.0;")],
     "clip_ignores_other_shards": [("or_clip_coef(q + other_sqnorm, h->max_grad_norm)",

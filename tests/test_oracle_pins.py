@@ -115,25 +115,59 @@ def test_reduce_rank_order():
 
 # ---------------------------------------------------------------- norm and clip
 
+def _exact_sq_sum(vals):
+    """Exact rational sum of squares of float32 values."""
+    return sum((Fraction(float(x)) ** 2 for x in vals), Fraction(0))
+
+
 def test_sqnorm_constant_closed_form():
-    c = np.float32(3 * 2.0 ** -10)
-    for n in (0, 1, 7, 100003):
-        g = np.full(n, c, np.float32)
-        assert O.sqnorm_accum(0.0, g) == n * float(c) ** 2
+    # c near 2: its squared significand is near 2^48, so more than 2^16 equal
+    # terms carry out of the low 64 bits of the accumulator
+    for c in (np.float32(3 * 2.0 ** -10), np.float32(1.9999999), np.float32(-1.5e-20)):
+        for n in (0, 1, 7, 100_003):
+            g = np.full(n, c, np.float32)
+            assert O.sqnorm(g) == float(n * Fraction(float(c)) ** 2)
 
 
-def test_sqnorm_against_fsum_and_chunking():
+def test_sqnorm_is_the_exactly_rounded_sum():
     rng = np.random.default_rng(4)
-    g = rng.normal(0, 1e-3, 200001).astype(np.float32)
-    q = O.sqnorm_accum(0.0, g)
-    ref = math.fsum(float(x) * float(x) for x in g)
-    assert abs(q - ref) <= g.size * 2.0 ** -53 * ref
-    # accumulating chunk after chunk in ascending order is the same sum
-    q2 = 0.0
-    for a in range(0, g.size, 65536):
-        q2 = O.sqnorm_accum(q2, g[a:a + 65536])
-    assert q2 == q
-    assert O.sqnorm_accum(1.5, g[:0]) == 1.5
+    g = rng.normal(0, 1e-3, 200_001).astype(np.float32)
+    g[::997] *= 1e3                         # outliers, as in the gradient workloads
+    q = O.sqnorm(g)
+    assert q == math.fsum(float(x) * float(x) for x in g)   # fsum: correctly rounded
+    # chunks added in any order give the same exactly rounded total
+    acc = O.SqAcc()
+    for a in range(0, g.size, 65_536)[::-1]:
+        acc.add(g[a:a + 65_536])
+    assert acc.value() == q
+    assert O.sqnorm(g[:0]) == 0.0
+
+
+def test_sqnorm_wide_range_and_subnormals():
+    vals = np.array([3.0e38, 1e-30, -2.0 ** -149, 2.0 ** -126, 1.0, -7.25, 2.0 ** -140,
+                     1e19, 5e-45], np.float32)
+    assert O.sqnorm(vals) == float(_exact_sq_sum(vals))
+    sub = np.array([2.0 ** -149] * 3, np.float32)      # squares far below fp32 range
+    assert O.sqnorm(sub) == 3 * 2.0 ** -298
+    rng = np.random.default_rng(44)
+    bits = rng.integers(0, 0x7F800000, size=2000, dtype=np.int64).astype(np.uint32)
+    x = bits.view(np.float32)
+    assert O.sqnorm(x) == float(_exact_sq_sum(x))
+
+
+def test_sqnorm_ties_round_to_even():
+    # 2^53 + 1 (in units of 2^-298... here units of 1): exactly between two doubles
+    one = np.float32(1.0)
+    big = np.full(1, np.float32(2.0 ** 26), np.float32)  # square 2^52
+    g = np.concatenate([big, big, np.array([one], np.float32)])   # 2^53 + 1
+    assert O.sqnorm(g) == 2.0 ** 53                                # tie -> even
+    g3 = np.concatenate([g, np.array([one, one], np.float32)])     # 2^53 + 3
+    assert O.sqnorm(g3) == 2.0 ** 53 + 4                           # tie -> even
+
+
+def test_sqnorm_non_finite():
+    assert np.isnan(O.sqnorm(np.array([1.0, np.nan, np.inf], np.float32)))
+    assert O.sqnorm(np.array([1.0, -np.inf], np.float32)) == np.inf
 
 
 @pytest.mark.parametrize("scale,max_norm", [(1e-3, 1.0), (1.0, 1.0), (3.0, 0.5),
@@ -147,10 +181,10 @@ def test_clip_against_clip_grad_norm(scale, max_norm):
         t.grad = torch.from_numpy(p.astype(np.float64))
     torch.nn.utils.clip_grad_norm_(tens, max_norm)
     torch_coef = tens[0].grad[0].item() / float(parts[0][0])
-    Q = 0.0
+    Q = O.SqAcc()
     for p in parts:
-        Q = O.sqnorm_accum(Q, p)
-    coef = O.clip_coef(Q, max_norm)
+        Q.add(p)
+    coef = O.clip_coef(Q.value(), max_norm)
     if torch_coef >= 1.0 - 1e-15:
         assert coef == np.float32(1.0)
     else:
@@ -488,7 +522,7 @@ def _ddp_vs_sharded(psi, n_d, align, h, grads_bf16, w0, m0, v0):
     for k in range(n_d):
         _, off, V = O.layout(psi, n_d, k, align, stage=2)
         g = O.reduce_mean([np.ascontiguousarray(gr[off:off + V]) for gr in grads_bf16])
-        q_parts.append(O.sqnorm_accum(0.0, g))
+        q_parts.append(O.sqnorm(g))
     Qtot = 0.0
     for q in q_parts:
         Qtot += q
