@@ -35,7 +35,33 @@ namespace zs {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStepMaxBlocks = 4096;
+
+// Launch shape (compile-time; a build may override them to sweep):
+// blocks in the grid-stride loops, and vectors of 8 parameters each lane
+// loads before it computes (more bytes in flight per lane).
+#ifndef ZS_STEP_BLOCKS
+#define ZS_STEP_BLOCKS 4096
+#endif
+#ifndef ZS_SQ_BLOCKS
+#define ZS_SQ_BLOCKS 4096
+#endif
+#ifndef ZS_STEP_UNROLL
+#define ZS_STEP_UNROLL 1
+#endif
+#ifndef ZS_SQ_UNROLL
+#define ZS_SQ_UNROLL 1
+#endif
+// Non-temporal (streaming) cache policy for loads / stores of data that is
+// touched once per step.
+#ifndef ZS_NT_LOAD
+#define ZS_NT_LOAD 0
+#endif
+#ifndef ZS_NT_STORE
+#define ZS_NT_STORE 0
+#endif
+constexpr int kStepMaxBlocks = ZS_STEP_BLOCKS;
+constexpr int kSqBlocks = ZS_SQ_BLOCKS;
+static_assert(ZS_SQ_BLOCKS <= kMaxSqnormBlocks, "partials must fit the workspace");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -72,6 +98,22 @@ struct SqArgs {
     float inv_nd;
 };
 
+// ---- streaming loads and stores -------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ T ld(const T* p)
+{
+    if constexpr (ZS_NT_LOAD) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, T v)
+{
+    if constexpr (ZS_NT_STORE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // ---- bf16 --------------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -79,11 +121,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 // fp32 -> bf16, round to nearest even: adding 0x7FFF plus the lowest kept
 // bit carries into the kept bits exactly when the dropped half is above one
-// half ulp, or equal to it with an odd kept value.  NaN -> sign | 0x7FC0.
+// half ulp, or equal to it with an odd kept value.  Every NaN becomes the
+// canonical 0x7FC0 (the sign of an arithmetic NaN is not defined by IEEE 754
+// and differs between processors).
 __device__ __forceinline__ uint32_t bf16_rne(float f)
 {
     const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
@@ -116,7 +160,7 @@ template <int NDT, typename Args>
 __device__ __forceinline__ void reduce_vec(const Args& a, int64_t vi, float g[8])
 {
     const int nd = NDT > 0 ? NDT : a.n_d;
-    const u32x4 x = reinterpret_cast<const u32x4*>(a.slices.p[0])[vi];
+    const u32x4 x = ld(reinterpret_cast<const u32x4*>(a.slices.p[0]) + vi);
     g[0] = bf16_lo(x.x); g[1] = bf16_hi(x.x);
     g[2] = bf16_lo(x.y); g[3] = bf16_hi(x.y);
     g[4] = bf16_lo(x.z); g[5] = bf16_hi(x.z);
@@ -128,7 +172,7 @@ __device__ __forceinline__ void reduce_vec(const Args& a, int64_t vi, float g[8]
         u32x4 b[G];
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            if (r0 + j < nd) b[j] = reinterpret_cast<const u32x4*>(a.slices.p[r0 + j])[vi];
+            if (r0 + j < nd) b[j] = ld(reinterpret_cast<const u32x4*>(a.slices.p[r0 + j]) + vi);
 #pragma unroll
         for (int j = 0; j < G; ++j)
             if (r0 + j < nd) add8(g, b[j]);
@@ -195,28 +239,42 @@ __device__ __forceinline__ double block_sum(double q)
 // ---- kernels ----------------------------------------------------------------------
 
 // Clip pass 1: mean of the slices (optionally stored) and one fp64 partial
-// sum of squares per block.
-template <int NDT, bool STORE>
-__global__ void __launch_bounds__(kThreads) k_reduce_sqnorm(const SqArgs a)
+// sum of squares per block.  A lane handles vectors vi, vi + stride, ... in
+// that order, U of them per iteration (all loads first); the order of its
+// fp64 additions does not depend on U.
+template <int U, int NDT, bool STORE>
+__device__ __forceinline__ void reduce_vectors(const SqArgs& a, int64_t vi, int64_t stride,
+                                               double& q)
 {
-    const int64_t nvec = a.valid_len >> 3;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    double q = 0.0;
-    for (int64_t vi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; vi < nvec;
-         vi += stride) {
-        float g[8];
-        reduce_vec<NDT>(a, vi, g);
+    float g[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) reduce_vec<NDT>(a, vi + u * stride, g[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
         if constexpr (STORE) {
-            f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
-            o[0] = f32x4{g[0], g[1], g[2], g[3]};
-            o[1] = f32x4{g[4], g[5], g[6], g[7]};
+            f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * (vi + u * stride);
+            st(o, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
+            st(o + 1, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const double d = g[j];
+            const double d = g[u][j];
             q = q + d * d;
         }
     }
+}
+
+template <int NDT, bool STORE>
+__global__ void __launch_bounds__(kThreads) k_reduce_sqnorm(const SqArgs a)
+{
+    constexpr int U = ZS_SQ_UNROLL;
+    const int64_t nvec = a.valid_len >> 3;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    double q = 0.0;
+    int64_t vi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    for (; vi + (U - 1) * stride < nvec; vi += U * stride)
+        reduce_vectors<U, NDT, STORE>(a, vi, stride, q);
+    for (; vi < nvec; vi += stride) reduce_vectors<1, NDT, STORE>(a, vi, stride, q);
     const int64_t tail0 = nvec * 8;
     if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < a.valid_len - tail0) {
         const int64_t i = tail0 + threadIdx.x;
@@ -240,51 +298,77 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // The fused step: gradient (mean of the slices, or the stored mean), clip,
-// AdamW in place, bf16 cast into the slot, zero pads.
+// AdamW in place, bf16 cast into the slot, zero pads.  A lane handles U
+// vectors (at vi, vi + stride, ...) per iteration, all loads first.
+template <int U, bool FROM_SLICES, int NDT, bool CLIP>
+__device__ __forceinline__ void step_vectors(const StepArgs& a, const StepConsts& c, float coef,
+                                             int64_t vi, int64_t stride)
+{
+    f32x4* w4 = reinterpret_cast<f32x4*>(a.w);
+    f32x4* m4 = reinterpret_cast<f32x4*>(a.m);
+    f32x4* v4 = reinterpret_cast<f32x4*>(a.v);
+    u32x4* o4 = reinterpret_cast<u32x4*>(a.out);
+    float g[U][8], W[U][8], M[U][8], V[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t x = vi + u * stride;
+        if constexpr (FROM_SLICES) {
+            reduce_vec<NDT>(a, x, g[u]);
+        } else {
+            const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * x;
+            const f32x4 x0 = ld(g4), x1 = ld(g4 + 1);
+            g[u][0] = x0.x; g[u][1] = x0.y; g[u][2] = x0.z; g[u][3] = x0.w;
+            g[u][4] = x1.x; g[u][5] = x1.y; g[u][6] = x1.z; g[u][7] = x1.w;
+        }
+        const f32x4 w0 = ld(w4 + 2 * x), w1 = ld(w4 + 2 * x + 1);
+        const f32x4 m0 = ld(m4 + 2 * x), m1 = ld(m4 + 2 * x + 1);
+        const f32x4 v0 = ld(v4 + 2 * x), v1 = ld(v4 + 2 * x + 1);
+        W[u][0] = w0.x; W[u][1] = w0.y; W[u][2] = w0.z; W[u][3] = w0.w;
+        W[u][4] = w1.x; W[u][5] = w1.y; W[u][6] = w1.z; W[u][7] = w1.w;
+        M[u][0] = m0.x; M[u][1] = m0.y; M[u][2] = m0.z; M[u][3] = m0.w;
+        M[u][4] = m1.x; M[u][5] = m1.y; M[u][6] = m1.z; M[u][7] = m1.w;
+        V[u][0] = v0.x; V[u][1] = v0.y; V[u][2] = v0.z; V[u][3] = v0.w;
+        V[u][4] = v1.x; V[u][5] = v1.y; V[u][6] = v1.z; V[u][7] = v1.w;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float gj = g[u][j];
+            if constexpr (CLIP) gj = gj * coef;
+            adamw1(c, gj, W[u][j], M[u][j], V[u][j]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t x = vi + u * stride;
+        st(w4 + 2 * x, f32x4{W[u][0], W[u][1], W[u][2], W[u][3]});
+        st(w4 + 2 * x + 1, f32x4{W[u][4], W[u][5], W[u][6], W[u][7]});
+        st(m4 + 2 * x, f32x4{M[u][0], M[u][1], M[u][2], M[u][3]});
+        st(m4 + 2 * x + 1, f32x4{M[u][4], M[u][5], M[u][6], M[u][7]});
+        st(v4 + 2 * x, f32x4{V[u][0], V[u][1], V[u][2], V[u][3]});
+        st(v4 + 2 * x + 1, f32x4{V[u][4], V[u][5], V[u][6], V[u][7]});
+        st(o4 + x, u32x4{pack_bf16x2(W[u][0], W[u][1]), pack_bf16x2(W[u][2], W[u][3]),
+                         pack_bf16x2(W[u][4], W[u][5]), pack_bf16x2(W[u][6], W[u][7])});
+    }
+}
+
 template <bool FROM_SLICES, int NDT, bool CLIP>
 __global__ void __launch_bounds__(kThreads) k_step(const StepArgs a)
 {
+    // Unrolling multiplies the registers of the slice loads; the bf16-slice
+    // source keeps one vector per iteration.
+    constexpr int U = FROM_SLICES ? 1 : ZS_STEP_UNROLL;
     float coef = 1.0f;
     if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
     const StepConsts c = a.c;
     const int64_t nvec = a.valid_len >> 3;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
     const int64_t gtid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    f32x4* w4 = reinterpret_cast<f32x4*>(a.w);
-    f32x4* m4 = reinterpret_cast<f32x4*>(a.m);
-    f32x4* v4 = reinterpret_cast<f32x4*>(a.v);
-    u32x4* o4 = reinterpret_cast<u32x4*>(a.out);
-    for (int64_t vi = gtid; vi < nvec; vi += stride) {
-        float g[8];
-        if constexpr (FROM_SLICES) {
-            reduce_vec<NDT>(a, vi, g);
-        } else {
-            const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * vi;
-            const f32x4 x0 = g4[0], x1 = g4[1];
-            g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w;
-            g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
-        }
-        const f32x4 w0 = w4[2 * vi], w1 = w4[2 * vi + 1];
-        const f32x4 m0 = m4[2 * vi], m1 = m4[2 * vi + 1];
-        const f32x4 v0 = v4[2 * vi], v1 = v4[2 * vi + 1];
-        float W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-        float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float gj = g[j];
-            if constexpr (CLIP) gj = gj * coef;
-            adamw1(c, gj, W[j], M[j], V[j]);
-        }
-        w4[2 * vi] = f32x4{W[0], W[1], W[2], W[3]};
-        w4[2 * vi + 1] = f32x4{W[4], W[5], W[6], W[7]};
-        m4[2 * vi] = f32x4{M[0], M[1], M[2], M[3]};
-        m4[2 * vi + 1] = f32x4{M[4], M[5], M[6], M[7]};
-        v4[2 * vi] = f32x4{V[0], V[1], V[2], V[3]};
-        v4[2 * vi + 1] = f32x4{V[4], V[5], V[6], V[7]};
-        o4[vi] = u32x4{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3]),
-                       pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])};
-    }
+    int64_t vi = gtid;
+    for (; vi + (U - 1) * stride < nvec; vi += U * stride)
+        step_vectors<U, FROM_SLICES, NDT, CLIP>(a, c, coef, vi, stride);
+    for (; vi < nvec; vi += stride) step_vectors<1, FROM_SLICES, NDT, CLIP>(a, c, coef, vi, stride);
     const int64_t tail0 = nvec * 8;
     if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < a.valid_len - tail0) {
         const int64_t i = tail0 + threadIdx.x;
@@ -436,7 +520,7 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     a.n_d = s->n_d;
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
-    const int blocks = grid_for(s->valid_len, s->valid_len, kMaxSqnormBlocks);
+    const int blocks = grid_for(s->valid_len, s->valid_len, kSqBlocks);
     (void)hipGetLastError();   // drop an error left by an unrelated earlier call
     hipStream_t st = static_cast<hipStream_t>(stream);
     launch_sqnorm(a, mean_out != nullptr, blocks, st);

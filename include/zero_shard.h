@@ -169,7 +169,7 @@ int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices, flo
  * shard_len - valid_len pad positions.  Nothing beyond valid_len is read or
  * written in the state or gradient buffers, and nothing outside this
  * rank's slot of the gather buffer is written.  bf16_rne: round to nearest
- * even; any NaN becomes sign|0x7FC0.
+ * even; any NaN becomes the canonical quiet NaN 0x7FC0.
  * Errors: ZS_ENULL, ZS_EINVAL_*, ZS_EALIGN, ZS_EUNSUPPORTED, ZS_ELAUNCH. */
 int zero_shard_step(const zs_shard* s, const zs_adamw* h, const uint16_t* const* grad_slices,
                     const float* mean_in, const double* sqnorm, double other_sqnorm,

@@ -110,7 +110,7 @@ uint16_t or_bf16_rne(float x)
 {
     uint32_t u = f32_bits(x);
     if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
-        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);   /* NaN */
+        return (uint16_t)0x7FC0u;   /* any NaN: the canonical quiet NaN */
     uint32_t hi = u >> 16;          /* kept: sign, exponent, 7 mantissa bits */
     uint32_t lo = u & 0xFFFFu;      /* dropped bits */
     /* Nearest; on an exact tie pick the even kept value.  A carry out of the

@@ -82,7 +82,9 @@ double or_hsdp_inter_bytes(double psi, int32_t n_d, int32_t g,
 /* ---- bfloat16 ------------------------------------------------------------ */
 /* [DPZ] §3 Notation: weights and gradients are bf16.  Reading: float->bf16 is
  * round to nearest, ties to even on the 16 dropped bits; +-Inf, +-0 kept;
- * overflow rounds to Inf; any NaN becomes the quiet NaN sign|0x7FC0. */
+ * overflow rounds to Inf; any NaN becomes the canonical quiet NaN 0x7FC0
+ * (IEEE 754 leaves the sign and payload of an arithmetic NaN open, so only
+ * a canonical NaN makes the packed bits well defined). */
 uint16_t or_bf16_rne(float x);
 float    or_bf16_to_f32(uint16_t h);   /* exact widening */
 void     or_bf16_rne_array(const float* x, int64_t n, uint16_t* out);

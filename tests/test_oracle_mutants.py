@@ -54,6 +54,7 @@ MUTANTS = {
     "bf16_ties_away": [("if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))",
                         "if (lo >= 0x8000u)")],
     "bf16_truncates": [("        hi += 1u;\n", "        hi += 0u;\n")],
+    "bf16_nan_keeps_sign": [("return (uint16_t)0x7FC0u;", "return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);")],
     "layout_offset_unpadded": [("off = (int64_t)rank * S;", "off = (int64_t)rank * chunk;")],
     "layout_no_align": [("S = ((chunk + align - 1) / align) * align;", "S = chunk;")],
     "zero2_state_drops_grad": [("case 2: return 2.0 * psi + (2.0 + K) * psi / n_d;",

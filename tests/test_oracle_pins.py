@@ -350,21 +350,24 @@ def test_bf16_rne_against_torch_structured_exhaustive():
     got = O.bf16_rne(x)
     ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     nan_in = np.isnan(x)
+    assert nan_in.sum() > 1000
+    # Finite values and infinities bit for bit.  torch's CPU cast is not
+    # consistent about NaN payloads (its vector path keeps high payload bits),
+    # so NaN is compared as a class; the reading fixes the canonical 0x7FC0.
     assert np.array_equal(got[~nan_in], ref[~nan_in])
-    # NaN stays NaN (class compare), quiet, sign kept
-    gnan = got[nan_in]
-    assert np.all((gnan & 0x7F80) == 0x7F80) and np.all((gnan & 0x0040) != 0)
-    assert np.array_equal(gnan >> 15, (bits[nan_in] >> 31).astype(np.uint16))
+    assert np.all((ref[nan_in] & 0x7F80) == 0x7F80) and np.all((ref[nan_in] & 0x7F) != 0)
+    assert np.all(got[nan_in] == 0x7FC0)
 
 
 def test_bf16_rne_random_against_torch():
     rng = np.random.default_rng(9)
     bits = rng.integers(0, 1 << 32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
     x = bits.view(np.float32)
-    x = x[~np.isnan(x)]
     got = O.bf16_rne(x)
     ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(got, ref)
+    nan_in = np.isnan(x)
+    assert np.array_equal(got[~nan_in], ref[~nan_in])
+    assert np.all(got[nan_in] == 0x7FC0)
 
 
 # -------------------------------------------------------------------- layout
