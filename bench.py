@@ -92,7 +92,8 @@ def cpu_baseline(wl, shard, seconds: float):
 
 
 def copy_ceiling(torch, nbytes=4 << 30, reps=10):
-    """Practical HBM bandwidth of a plain 16-byte-vector copy (read+write)."""
+    """Practical HBM bandwidth of a plain 16-byte-vector copy (read+write),
+    launched one-shot (the launch shape that copies fastest on MI355X)."""
     import ctypes as C
     lib = C.CDLL(os.path.join(ROOT, "fsdp_sharded_optimizer_zero_amd", "libzs_benchcopy.so"))
     lib.zs_bench_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
@@ -102,7 +103,7 @@ def copy_ceiling(torch, nbytes=4 << 30, reps=10):
     src.fill_(1)
     st = torch.cuda.current_stream()
     n16 = nbytes // 16
-    blocks = 256 * 16
+    blocks = (n16 + 255) // 256         # one-shot: one 16-byte vector per thread
     best = None
     for _ in range(2):
         assert lib.zs_bench_copy(src.data_ptr(), dst.data_ptr(), n16, blocks, st.cuda_stream) == 0

@@ -102,9 +102,12 @@ int zs_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align, int32_t sta
     return ZS_OK;
 }
 
-size_t zs_workspace_bytes(const zs_shard* /*s*/)
+size_t zs_workspace_bytes(const zs_shard* s)
 {
-    return static_cast<size_t>(zs::kMaxSqnormBlocks) * sizeof(double);
+    // One fp64 partial per clip-pass block, rounded up to 256 bytes.
+    const int64_t v = (s && s->valid_len > 0) ? s->valid_len : 0;
+    const int64_t bytes = zs::sq_blocks(v) * static_cast<int64_t>(sizeof(double));
+    return static_cast<size_t>(zs::round_up(bytes > 0 ? bytes : 1, 256));
 }
 
 double zs_state_bytes(double psi, int32_t n_d, int32_t stage, double K)

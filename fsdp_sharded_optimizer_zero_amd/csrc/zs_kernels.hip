@@ -2,11 +2,15 @@
 // the C-ABI entry points that validate arguments and launch them.
 //
 // Every kernel is a streaming, HBM-bound, elementwise pass (nothing here is
-// a contraction, so no MFMA): 64-lane waves, 256-thread blocks, each lane
-// owns 8 consecutive parameters per iteration so that every operand moves as
-// one 16-byte load or store (8 bf16 = 16 B, 8 fp32 = 2 x 16 B), and a
-// grid-stride loop covers shards of any length.  A tail shorter than 8
-// elements and the bf16 pads are handled by separate scalar loops.
+// a contraction, so no MFMA): 64-lane waves, each lane owns 8 consecutive
+// parameters so that every operand moves as one 16-byte load or store
+// (8 bf16 = 16 B, 8 fp32 = 2 x 16 B).  Grids are one-shot: one thread per
+// 8-parameter vector and hundreds of thousands of blocks, dispatched in
+// index order, so the addresses in flight form one window that sweeps the
+// arrays front to back (on MI355X this streams at ~6.3-6.9 TB/s, where a
+// persistent grid-stride loop levels off near 5 TB/s).  The last vector of
+// a shard may be partial; it and the bf16 pads are handled element by
+// element by the thread that owns it.
 //
 // What is computed ("Data parallelism, ZeRO and FSDP", Lesson 8):
 //  - the reduce-scatter's local reduction: the rank gradients are averaged
@@ -26,6 +30,7 @@
 // written operation), default IEEE division and square root.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -34,37 +39,68 @@
 namespace zs {
 namespace {
 
-constexpr int kThreads = 256;
-
-// Launch shape (compile-time; a build may override them to sweep):
-// blocks in the grid-stride loops, and vectors of 8 parameters each lane
-// loads before it computes (more bytes in flight per lane).
-#ifndef ZS_STEP_BLOCKS
-#define ZS_STEP_BLOCKS 4096
+// Launch shape of the step and the pack (a build may override it): threads
+// per block and 8-parameter vectors per thread.  The clip pass's shape is in
+// zs_internal.h because the workspace size depends on it.
+#ifndef ZS_STEP_BS
+#define ZS_STEP_BS 256
 #endif
-#ifndef ZS_SQ_BLOCKS
-#define ZS_SQ_BLOCKS 4096
+#ifndef ZS_STEP_U
+#define ZS_STEP_U 1
 #endif
-#ifndef ZS_STEP_UNROLL
-#define ZS_STEP_UNROLL 1
+// Blocks of the step / of the clip pass that may be resident on one CU at
+// a time (0: no cap).  A dynamic LDS reservation enforces the cap.  Few
+// resident waves keep the window of addresses in flight narrow, which suits
+// the HBM better than a full CU when 4 to 9 arrays stream at once.  Measured
+// on MI355X over an 875M-parameter shard: the step is ~7% faster at two
+// 256-thread blocks per CU than uncapped (one block leaves its division and
+// square-root chain exposed), the clip pass ~4% faster at one 512-thread
+// block per CU.
+#ifndef ZS_STEP_PER_CU
+#define ZS_STEP_PER_CU 2
 #endif
-#ifndef ZS_SQ_UNROLL
-#define ZS_SQ_UNROLL 1
+#ifndef ZS_SQ_PER_CU
+#define ZS_SQ_PER_CU 1
 #endif
-// Non-temporal (streaming) cache policy for loads / stores of data that is
-// touched once per step.
-#ifndef ZS_NT_LOAD
-#define ZS_NT_LOAD 0
+// Non-temporal (streaming) cache policy: stores of the step; loads and
+// stores of the clip pass.  Every byte here is touched once per pass.
+#ifndef ZS_STEP_NT_STORE
+#define ZS_STEP_NT_STORE 1
 #endif
-#ifndef ZS_NT_STORE
-#define ZS_NT_STORE 0
+#ifndef ZS_SQ_NT_LOAD
+#define ZS_SQ_NT_LOAD 1
 #endif
-constexpr int kStepMaxBlocks = ZS_STEP_BLOCKS;
-constexpr int kSqBlocks = ZS_SQ_BLOCKS;
-static_assert(ZS_SQ_BLOCKS <= kMaxSqnormBlocks, "partials must fit the workspace");
+#ifndef ZS_SQ_NT_STORE
+#define ZS_SQ_NT_STORE 1
+#endif
+constexpr int kStepThreads = ZS_STEP_BS;
+constexpr int kStepU = ZS_STEP_U;
+constexpr bool kStepNtStore = ZS_STEP_NT_STORE != 0;
+constexpr bool kSqNtLoad = ZS_SQ_NT_LOAD != 0;
+constexpr bool kSqNtStore = ZS_SQ_NT_STORE != 0;
+constexpr int64_t kStepVecPerBlock = static_cast<int64_t>(ZS_STEP_BS) * ZS_STEP_U;
+constexpr int kFinalThreads = 1024;
+// Blocks of one launch at most; a longer shard takes several launches
+// (2^24 blocks of 256 vectors of 8 cover 3.4e10 parameters).
+constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 24;
+constexpr int kMaxDevices = 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT, typename T>
+__device__ __forceinline__ T load(const T* p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ void store(T* p, T v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 struct SlicePtrs {
     const uint16_t* p[ZS_MAX_RANKS];
@@ -82,6 +118,7 @@ struct StepArgs {
     uint16_t* out;          // slot base: shard element 0
     int64_t valid_len;
     int64_t shard_len;
+    int64_t v0;             // first vector of this launch
     int32_t n_d;
     float nd;               // (float)n_d
     float inv_nd;           // 1/n_d, exact when n_d is a power of two
@@ -91,28 +128,13 @@ struct StepArgs {
 struct SqArgs {
     SlicePtrs slices;
     float* mean_out;
-    double* partials;
+    double* partials;       // one per block of this launch
     int64_t valid_len;
+    int64_t v0;             // first vector of this launch
     int32_t n_d;
     float nd;
     float inv_nd;
 };
-
-// ---- streaming loads and stores -------------------------------------------------
-
-template <typename T>
-__device__ __forceinline__ T ld(const T* p)
-{
-    if constexpr (ZS_NT_LOAD) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-
-template <typename T>
-__device__ __forceinline__ void st(T* p, T v)
-{
-    if constexpr (ZS_NT_STORE) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
 
 // ---- bf16 --------------------------------------------------------------------
 
@@ -156,11 +178,11 @@ __device__ __forceinline__ float mean_of_sum(float s, float nd, float inv_nd)
 }
 
 // Mean of 8 consecutive elements (vector vi) over the ranks, in rank order.
-template <int NDT, typename Args>
+template <int NDT, bool NTL = false, typename Args>
 __device__ __forceinline__ void reduce_vec(const Args& a, int64_t vi, float g[8])
 {
     const int nd = NDT > 0 ? NDT : a.n_d;
-    const u32x4 x = ld(reinterpret_cast<const u32x4*>(a.slices.p[0]) + vi);
+    const u32x4 x = load<NTL>(reinterpret_cast<const u32x4*>(a.slices.p[0]) + vi);
     g[0] = bf16_lo(x.x); g[1] = bf16_hi(x.x);
     g[2] = bf16_lo(x.y); g[3] = bf16_hi(x.y);
     g[4] = bf16_lo(x.z); g[5] = bf16_hi(x.z);
@@ -172,7 +194,7 @@ __device__ __forceinline__ void reduce_vec(const Args& a, int64_t vi, float g[8]
         u32x4 b[G];
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            if (r0 + j < nd) b[j] = ld(reinterpret_cast<const u32x4*>(a.slices.p[r0 + j]) + vi);
+            if (r0 + j < nd) b[j] = load<NTL>(reinterpret_cast<const u32x4*>(a.slices.p[r0 + j]) + vi);
 #pragma unroll
         for (int j = 0; j < G; ++j)
             if (r0 + j < nd) add8(g, b[j]);
@@ -217,13 +239,14 @@ __device__ __forceinline__ float clip_coef(double Q, double max_norm)
 
 // ---- deterministic fp64 block sum (result valid in thread 0) ------------------
 
+template <int BS>
 __device__ __forceinline__ double block_sum(double q)
 {
     // xor butterfly: both partners add the same two values, so every lane
     // ends with the same bits.
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) q = q + __shfl_xor(q, off, 64);
-    __shared__ double wave_sums[kThreads / 64];
+    __shared__ double wave_sums[BS / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) wave_sums[wave] = q;
     __syncthreads();
@@ -231,7 +254,7 @@ __device__ __forceinline__ double block_sum(double q)
     if (threadIdx.x == 0) {
         t = wave_sums[0];
 #pragma unroll
-        for (int k = 1; k < kThreads / 64; ++k) t = t + wave_sums[k];
+        for (int k = 1; k < BS / 64; ++k) t = t + wave_sums[k];
     }
     return t;
 }
@@ -239,70 +262,99 @@ __device__ __forceinline__ double block_sum(double q)
 // ---- kernels ----------------------------------------------------------------------
 
 // Clip pass 1: mean of the slices (optionally stored) and one fp64 partial
-// sum of squares per block.  A lane handles vectors vi, vi + stride, ... in
-// that order, U of them per iteration (all loads first); the order of its
-// fp64 additions does not depend on U.
-template <int U, int NDT, bool STORE>
-__device__ __forceinline__ void reduce_vectors(const SqArgs& a, int64_t vi, int64_t stride,
-                                               double& q)
-{
-    float g[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) reduce_vec<NDT>(a, vi + u * stride, g[u]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if constexpr (STORE) {
-            f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * (vi + u * stride);
-            st(o, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
-            st(o + 1, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const double d = g[u][j];
-            q = q + d * d;
-        }
-    }
-}
-
+// sum of squares per block.  Block b of a launch owns kSqVecPerBlock
+// consecutive vectors; thread x reduces vectors base + u*BS + x, u = 0..U-1,
+// issuing all their loads first, and adds their squares in u, then element
+// order.  Only the last block of a shard meets the partial vector or runs
+// past valid_len; it takes the guarded path.
 template <int NDT, bool STORE>
-__global__ void __launch_bounds__(kThreads) k_reduce_sqnorm(const SqArgs a)
+__global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
 {
-    constexpr int U = ZS_SQ_UNROLL;
-    const int64_t nvec = a.valid_len >> 3;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    constexpr int BS = kSqThreads, U = ZS_SQ_U;
+    const int64_t nfull = a.valid_len >> 3;
+    const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kSqVecPerBlock;
     double q = 0.0;
-    int64_t vi = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    for (; vi + (U - 1) * stride < nvec; vi += U * stride)
-        reduce_vectors<U, NDT, STORE>(a, vi, stride, q);
-    for (; vi < nvec; vi += stride) reduce_vectors<1, NDT, STORE>(a, vi, stride, q);
-    const int64_t tail0 = nvec * 8;
-    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < a.valid_len - tail0) {
-        const int64_t i = tail0 + threadIdx.x;
-        const float g = reduce_one<NDT>(a, i);
-        if constexpr (STORE) a.mean_out[i] = g;
-        const double d = g;
-        q = q + d * d;
+    if (base + kSqVecPerBlock <= nfull) {
+        float g[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) reduce_vec<NDT, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vi = base + u * BS + threadIdx.x;
+            if constexpr (STORE) {
+                f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
+                store<kSqNtStore>(o, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
+                store<kSqNtStore>(o + 1, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double d = g[u][j];
+                q = q + d * d;
+            }
+        }
+    } else {
+        for (int u = 0; u < U; ++u) {
+            const int64_t vi = base + u * BS + threadIdx.x;
+            if (vi < nfull) {
+                float g[8];
+                reduce_vec<NDT, kSqNtLoad>(a, vi, g);
+                if constexpr (STORE) {
+                    f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
+                    store<kSqNtStore>(o, f32x4{g[0], g[1], g[2], g[3]});
+                    store<kSqNtStore>(o + 1, f32x4{g[4], g[5], g[6], g[7]});
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const double d = g[j];
+                    q = q + d * d;
+                }
+            } else if (vi == nfull) {
+                for (int64_t i = vi * 8; i < a.valid_len; ++i) {
+                    const float g = reduce_one<NDT>(a, i);
+                    if constexpr (STORE) a.mean_out[i] = g;
+                    const double d = g;
+                    q = q + d * d;
+                }
+            }
+        }
     }
-    const double t = block_sum(q);
+    const double t = block_sum<BS>(q);
     if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
 }
 
-// Clip pass 2: sum the block partials in a fixed order.
-__global__ void __launch_bounds__(kThreads)
-    k_sqnorm_final(const double* partials, int n, double* out, int accumulate)
+// Clip pass 2: sum the n block partials in a fixed order (thread x takes
+// x, x + 1024, ... in order; then the block tree).
+__global__ void __launch_bounds__(kFinalThreads)
+    k_sqnorm_final(const double* partials, int64_t n, double* out, int accumulate)
 {
     double q = 0.0;
-    for (int i = threadIdx.x; i < n; i += kThreads) q = q + partials[i];
-    const double t = block_sum(q);
+    for (int64_t i = threadIdx.x; i < n; i += kFinalThreads) q = q + partials[i];
+    const double t = block_sum<kFinalThreads>(q);
     if (threadIdx.x == 0) *out = accumulate ? (*out + t) : t;
 }
 
-// The fused step: gradient (mean of the slices, or the stored mean), clip,
-// AdamW in place, bf16 cast into the slot, zero pads.  A lane handles U
-// vectors (at vi, vi + stride, ...) per iteration, all loads first.
-template <int U, bool FROM_SLICES, int NDT, bool CLIP>
+// One element of the step (the partial last vector).
+template <bool FROM_SLICES, int NDT, bool CLIP>
+__device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c, float coef,
+                                         int64_t i)
+{
+    float g;
+    if constexpr (FROM_SLICES) g = reduce_one<NDT>(a, i);
+    else g = a.mean[i];
+    if constexpr (CLIP) g = g * coef;
+    float w = a.w[i], m = a.m[i], v = a.v[i];
+    adamw1(c, g, w, m, v);
+    a.w[i] = w;
+    a.m[i] = m;
+    a.v[i] = v;
+    a.out[i] = static_cast<uint16_t>(bf16_rne(w));
+}
+
+// U full vectors at vi, vi + BS, ...: all loads, then the arithmetic, then
+// all stores.
+template <int U, int BS, bool FROM_SLICES, int NDT, bool CLIP>
 __device__ __forceinline__ void step_vectors(const StepArgs& a, const StepConsts& c, float coef,
-                                             int64_t vi, int64_t stride)
+                                             int64_t vi)
 {
     f32x4* w4 = reinterpret_cast<f32x4*>(a.w);
     f32x4* m4 = reinterpret_cast<f32x4*>(a.m);
@@ -311,18 +363,18 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, const StepConsts
     float g[U][8], W[U][8], M[U][8], V[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t x = vi + u * stride;
+        const int64_t x = vi + u * BS;
         if constexpr (FROM_SLICES) {
             reduce_vec<NDT>(a, x, g[u]);
         } else {
             const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * x;
-            const f32x4 x0 = ld(g4), x1 = ld(g4 + 1);
+            const f32x4 x0 = g4[0], x1 = g4[1];
             g[u][0] = x0.x; g[u][1] = x0.y; g[u][2] = x0.z; g[u][3] = x0.w;
             g[u][4] = x1.x; g[u][5] = x1.y; g[u][6] = x1.z; g[u][7] = x1.w;
         }
-        const f32x4 w0 = ld(w4 + 2 * x), w1 = ld(w4 + 2 * x + 1);
-        const f32x4 m0 = ld(m4 + 2 * x), m1 = ld(m4 + 2 * x + 1);
-        const f32x4 v0 = ld(v4 + 2 * x), v1 = ld(v4 + 2 * x + 1);
+        const f32x4 w0 = w4[2 * x], w1 = w4[2 * x + 1];
+        const f32x4 m0 = m4[2 * x], m1 = m4[2 * x + 1];
+        const f32x4 v0 = v4[2 * x], v1 = v4[2 * x + 1];
         W[u][0] = w0.x; W[u][1] = w0.y; W[u][2] = w0.z; W[u][3] = w0.w;
         W[u][4] = w1.x; W[u][5] = w1.y; W[u][6] = w1.z; W[u][7] = w1.w;
         M[u][0] = m0.x; M[u][1] = m0.y; M[u][2] = m0.z; M[u][3] = m0.w;
@@ -341,86 +393,73 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, const StepConsts
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t x = vi + u * stride;
-        st(w4 + 2 * x, f32x4{W[u][0], W[u][1], W[u][2], W[u][3]});
-        st(w4 + 2 * x + 1, f32x4{W[u][4], W[u][5], W[u][6], W[u][7]});
-        st(m4 + 2 * x, f32x4{M[u][0], M[u][1], M[u][2], M[u][3]});
-        st(m4 + 2 * x + 1, f32x4{M[u][4], M[u][5], M[u][6], M[u][7]});
-        st(v4 + 2 * x, f32x4{V[u][0], V[u][1], V[u][2], V[u][3]});
-        st(v4 + 2 * x + 1, f32x4{V[u][4], V[u][5], V[u][6], V[u][7]});
-        st(o4 + x, u32x4{pack_bf16x2(W[u][0], W[u][1]), pack_bf16x2(W[u][2], W[u][3]),
-                         pack_bf16x2(W[u][4], W[u][5]), pack_bf16x2(W[u][6], W[u][7])});
+        const int64_t x = vi + u * BS;
+        constexpr bool NT = kStepNtStore;
+        store<NT>(w4 + 2 * x, f32x4{W[u][0], W[u][1], W[u][2], W[u][3]});
+        store<NT>(w4 + 2 * x + 1, f32x4{W[u][4], W[u][5], W[u][6], W[u][7]});
+        store<NT>(m4 + 2 * x, f32x4{M[u][0], M[u][1], M[u][2], M[u][3]});
+        store<NT>(m4 + 2 * x + 1, f32x4{M[u][4], M[u][5], M[u][6], M[u][7]});
+        store<NT>(v4 + 2 * x, f32x4{V[u][0], V[u][1], V[u][2], V[u][3]});
+        store<NT>(v4 + 2 * x + 1, f32x4{V[u][4], V[u][5], V[u][6], V[u][7]});
+        store<NT>(o4 + x, u32x4{pack_bf16x2(W[u][0], W[u][1]), pack_bf16x2(W[u][2], W[u][3]),
+                                pack_bf16x2(W[u][4], W[u][5]), pack_bf16x2(W[u][6], W[u][7])});
     }
 }
 
+// The fused step over the slot's shard_len/8 vectors: gradient (mean of the
+// slices, or the stored mean), clip, AdamW in place, bf16 cast into the
+// slot; vectors past valid_len are pads and get +0.  Block b of a launch
+// owns kStepVecPerBlock consecutive vectors.
 template <bool FROM_SLICES, int NDT, bool CLIP>
-__global__ void __launch_bounds__(kThreads) k_step(const StepArgs a)
+__global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
 {
-    // Unrolling multiplies the registers of the slice loads; the bf16-slice
-    // source keeps one vector per iteration.
-    constexpr int U = FROM_SLICES ? 1 : ZS_STEP_UNROLL;
+    constexpr int BS = kStepThreads, U = kStepU;
     float coef = 1.0f;
     if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
     const StepConsts c = a.c;
-    const int64_t nvec = a.valid_len >> 3;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    int64_t vi = gtid;
-    for (; vi + (U - 1) * stride < nvec; vi += U * stride)
-        step_vectors<U, FROM_SLICES, NDT, CLIP>(a, c, coef, vi, stride);
-    for (; vi < nvec; vi += stride) step_vectors<1, FROM_SLICES, NDT, CLIP>(a, c, coef, vi, stride);
-    const int64_t tail0 = nvec * 8;
-    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < a.valid_len - tail0) {
-        const int64_t i = tail0 + threadIdx.x;
-        float g;
-        if constexpr (FROM_SLICES) g = reduce_one<NDT>(a, i);
-        else g = a.mean[i];
-        if constexpr (CLIP) g = g * coef;
-        float w = a.w[i], m = a.m[i], v = a.v[i];
-        adamw1(c, g, w, m, v);
-        a.w[i] = w;
-        a.m[i] = m;
-        a.v[i] = v;
-        a.out[i] = static_cast<uint16_t>(bf16_rne(w));
+    const int64_t nfull = a.valid_len >> 3;
+    const int64_t nslot = a.shard_len >> 3;
+    const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kStepVecPerBlock;
+    if (base + kStepVecPerBlock <= nfull) {
+        step_vectors<U, BS, FROM_SLICES, NDT, CLIP>(a, c, coef, base + threadIdx.x);
+        return;
     }
-    for (int64_t i = a.valid_len + gtid; i < a.shard_len; i += stride) a.out[i] = 0;
+    for (int u = 0; u < U; ++u) {
+        const int64_t vi = base + u * BS + threadIdx.x;
+        if (vi < nfull) {
+            step_vectors<1, BS, FROM_SLICES, NDT, CLIP>(a, c, coef, vi);
+        } else if (vi < nslot) {
+            // The partial vector (its valid elements), then pads.
+            int64_t i = vi * 8;
+            for (; i < a.valid_len; ++i) step_one<FROM_SLICES, NDT, CLIP>(a, c, coef, i);
+            if (i == vi * 8) {
+                reinterpret_cast<u32x4*>(a.out)[vi] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                for (; i < vi * 8 + 8; ++i) a.out[i] = 0;
+            }
+        }
+    }
 }
 
-// Cast and pack only.
-__global__ void __launch_bounds__(kThreads)
-    k_pack(const float* w, uint16_t* out, int64_t valid_len, int64_t shard_len)
+// Cast and pack only: vector vi of the slot, one per thread.
+__global__ void __launch_bounds__(kStepThreads)
+    k_pack(const float* w, uint16_t* out, int64_t valid_len, int64_t shard_len, int64_t v0)
 {
-    const int64_t nvec = valid_len >> 3;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    const int64_t gtid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-    const f32x4* w4 = reinterpret_cast<const f32x4*>(w);
-    u32x4* o4 = reinterpret_cast<u32x4*>(out);
-    for (int64_t vi = gtid; vi < nvec; vi += stride) {
+    const int64_t vi = v0 + static_cast<int64_t>(blockIdx.x) * kStepThreads + threadIdx.x;
+    const int64_t nfull = valid_len >> 3;
+    if (vi < nfull) {
+        const f32x4* w4 = reinterpret_cast<const f32x4*>(w);
         const f32x4 a = w4[2 * vi], b = w4[2 * vi + 1];
-        o4[vi] = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                       pack_bf16x2(b.z, b.w)};
+        reinterpret_cast<u32x4*>(out)[vi] =
+            u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
+                  pack_bf16x2(b.z, b.w)};
+    } else if (vi < (shard_len >> 3)) {
+        for (int64_t i = vi * 8; i < vi * 8 + 8; ++i)
+            out[i] = i < valid_len ? static_cast<uint16_t>(bf16_rne(w[i])) : uint16_t(0);
     }
-    const int64_t tail0 = nvec * 8;
-    if (blockIdx.x == 0 && static_cast<int64_t>(threadIdx.x) < valid_len - tail0) {
-        const int64_t i = tail0 + threadIdx.x;
-        out[i] = static_cast<uint16_t>(bf16_rne(w[i]));
-    }
-    for (int64_t i = valid_len + gtid; i < shard_len; i += stride) out[i] = 0;
 }
 
 // ---- launch helpers -----------------------------------------------------------------
-
-int grid_for(int64_t valid_len, int64_t shard_len, int cap)
-{
-    const int64_t nvec = valid_len >> 3;
-    int64_t blocks = (nvec + kThreads - 1) / kThreads;
-    const int64_t pads = shard_len - valid_len;
-    const int64_t pad_blocks = (pads + kThreads - 1) / kThreads;
-    if (pad_blocks > blocks) blocks = pad_blocks;
-    if (blocks < 1) blocks = 1;
-    if (blocks > cap) blocks = cap;
-    return static_cast<int>(blocks);
-}
 
 bool is_pow2(int32_t n) { return n > 0 && (n & (n - 1)) == 0; }
 
@@ -429,49 +468,113 @@ int launched()
     return hipGetLastError() == hipSuccess ? ZS_OK : ZS_ELAUNCH;
 }
 
-template <int NDT>
-void launch_sqnorm_nd(const SqArgs& a, bool store, int blocks, hipStream_t st)
+// ---- residency cap ----------------------------------------------------------------
+
+// LDS bytes per CU of device `dev` (cached; 160 KB on gfx950).
+int device_lds_per_cu(int dev)
 {
-    if (store) hipLaunchKernelGGL((k_reduce_sqnorm<NDT, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_reduce_sqnorm<NDT, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+    static std::atomic<int> cache[kMaxDevices];
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess || v <= 0)
+            return -1;
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
 }
 
-void launch_sqnorm(const SqArgs& a, bool store, int blocks, hipStream_t st)
+// Dynamic LDS to request with each launch of kernel K so that at most
+// per_cu of its blocks fit on one CU (K itself uses < 1 KB of static LDS).
+// per_cu <= 0: no reservation.  Reservations above the default 64 KB per
+// block are enabled once per device with hipFuncSetAttribute.
+template <auto K>
+int lds_reservation(int per_cu, size_t* bytes)
+{
+    *bytes = 0;
+    if (per_cu <= 0) return ZS_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ZS_ELAUNCH;
+    const int lds_cu = device_lds_per_cu(dev);
+    if (lds_cu <= 0) return ZS_ELAUNCH;
+    const int64_t b = (static_cast<int64_t>(lds_cu) / per_cu) / 1024 * 1024 - 1024;
+    if (b <= 0) return ZS_OK;
+    if (b > 65536) {
+        static std::atomic<uint64_t> enabled{0};
+        const uint64_t bit = uint64_t(1) << dev;
+        if ((enabled.load(std::memory_order_relaxed) & bit) == 0) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(K),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    static_cast<int>(b)) != hipSuccess)
+                return ZS_ELAUNCH;
+            enabled.fetch_or(bit, std::memory_order_relaxed);
+        }
+    }
+    *bytes = static_cast<size_t>(b);
+    return ZS_OK;
+}
+
+template <int NDT, bool STORE>
+int launch_sqnorm_k(const SqArgs& a, int64_t blocks, hipStream_t st)
+{
+    size_t lds = 0;
+    const int rc = lds_reservation<k_reduce_sqnorm<NDT, STORE>>(ZS_SQ_PER_CU, &lds);
+    if (rc != ZS_OK) return rc;
+    hipLaunchKernelGGL((k_reduce_sqnorm<NDT, STORE>), dim3(blocks), dim3(kSqThreads), lds, st, a);
+    return launched();
+}
+
+template <int NDT>
+int launch_sqnorm_nd(const SqArgs& a, bool store, int64_t blocks, hipStream_t st)
+{
+    return store ? launch_sqnorm_k<NDT, true>(a, blocks, st)
+                 : launch_sqnorm_k<NDT, false>(a, blocks, st);
+}
+
+int launch_sqnorm(const SqArgs& a, bool store, int64_t blocks, hipStream_t st)
 {
     switch (a.n_d) {
-    case 1: launch_sqnorm_nd<1>(a, store, blocks, st); break;
-    case 2: launch_sqnorm_nd<2>(a, store, blocks, st); break;
-    case 4: launch_sqnorm_nd<4>(a, store, blocks, st); break;
-    case 8: launch_sqnorm_nd<8>(a, store, blocks, st); break;
-    case 16: launch_sqnorm_nd<16>(a, store, blocks, st); break;
-    case 32: launch_sqnorm_nd<32>(a, store, blocks, st); break;
-    case 64: launch_sqnorm_nd<64>(a, store, blocks, st); break;
-    default: launch_sqnorm_nd<0>(a, store, blocks, st); break;
+    case 1: return launch_sqnorm_nd<1>(a, store, blocks, st);
+    case 2: return launch_sqnorm_nd<2>(a, store, blocks, st);
+    case 4: return launch_sqnorm_nd<4>(a, store, blocks, st);
+    case 8: return launch_sqnorm_nd<8>(a, store, blocks, st);
+    case 16: return launch_sqnorm_nd<16>(a, store, blocks, st);
+    case 32: return launch_sqnorm_nd<32>(a, store, blocks, st);
+    case 64: return launch_sqnorm_nd<64>(a, store, blocks, st);
+    default: return launch_sqnorm_nd<0>(a, store, blocks, st);
     }
+}
+
+template <bool FROM_SLICES, int NDT, bool CLIP>
+int launch_step_k(const StepArgs& a, int64_t blocks, hipStream_t st)
+{
+    size_t lds = 0;
+    const int rc = lds_reservation<k_step<FROM_SLICES, NDT, CLIP>>(ZS_STEP_PER_CU, &lds);
+    if (rc != ZS_OK) return rc;
+    hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, CLIP>), dim3(blocks), dim3(kStepThreads), lds,
+                       st, a);
+    return launched();
 }
 
 template <bool FROM_SLICES, int NDT>
-void launch_step_nd(const StepArgs& a, bool clip, int blocks, hipStream_t st)
+int launch_step_nd(const StepArgs& a, bool clip, int64_t blocks, hipStream_t st)
 {
-    if (clip) hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+    return clip ? launch_step_k<FROM_SLICES, NDT, true>(a, blocks, st)
+                : launch_step_k<FROM_SLICES, NDT, false>(a, blocks, st);
 }
 
-void launch_step(const StepArgs& a, bool from_slices, bool clip, int blocks, hipStream_t st)
+int launch_step(const StepArgs& a, bool from_slices, bool clip, int64_t blocks, hipStream_t st)
 {
-    if (!from_slices) {
-        launch_step_nd<false, 0>(a, clip, blocks, st);
-        return;
-    }
+    if (!from_slices) return launch_step_nd<false, 0>(a, clip, blocks, st);
     switch (a.n_d) {
-    case 1: launch_step_nd<true, 1>(a, clip, blocks, st); break;
-    case 2: launch_step_nd<true, 2>(a, clip, blocks, st); break;
-    case 4: launch_step_nd<true, 4>(a, clip, blocks, st); break;
-    case 8: launch_step_nd<true, 8>(a, clip, blocks, st); break;
-    case 16: launch_step_nd<true, 16>(a, clip, blocks, st); break;
-    case 32: launch_step_nd<true, 32>(a, clip, blocks, st); break;
-    case 64: launch_step_nd<true, 64>(a, clip, blocks, st); break;
-    default: launch_step_nd<true, 0>(a, clip, blocks, st); break;
+    case 1: return launch_step_nd<true, 1>(a, clip, blocks, st);
+    case 2: return launch_step_nd<true, 2>(a, clip, blocks, st);
+    case 4: return launch_step_nd<true, 4>(a, clip, blocks, st);
+    case 8: return launch_step_nd<true, 8>(a, clip, blocks, st);
+    case 16: return launch_step_nd<true, 16>(a, clip, blocks, st);
+    case 32: return launch_step_nd<true, 32>(a, clip, blocks, st);
+    case 64: return launch_step_nd<true, 64>(a, clip, blocks, st);
+    default: return launch_step_nd<true, 0>(a, clip, blocks, st);
     }
 }
 
@@ -520,13 +623,18 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     a.n_d = s->n_d;
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
-    const int blocks = grid_for(s->valid_len, s->valid_len, kSqBlocks);
+    const int64_t blocks = sq_blocks(s->valid_len);
     (void)hipGetLastError();   // drop an error left by an unrelated earlier call
     hipStream_t st = static_cast<hipStream_t>(stream);
-    launch_sqnorm(a, mean_out != nullptr, blocks, st);
-    if ((rc = launched()) != ZS_OK) return rc;
-    hipLaunchKernelGGL(k_sqnorm_final, dim3(1), dim3(kThreads), 0, st,
-                       static_cast<const double*>(workspace), blocks, sqnorm_out,
+    double* partials = static_cast<double*>(workspace);
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        a.v0 = b0 * kSqVecPerBlock;
+        a.partials = partials + b0;
+        if ((rc = launch_sqnorm(a, mean_out != nullptr, nb, st)) != ZS_OK) return rc;
+    }
+    hipLaunchKernelGGL(k_sqnorm_final, dim3(1), dim3(kFinalThreads), 0, st,
+                       static_cast<const double*>(partials), blocks, sqnorm_out,
                        accumulate ? 1 : 0);
     return launched();
 }
@@ -575,10 +683,15 @@ extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
     a.c = make_consts(h);
-    const int blocks = grid_for(s->valid_len, s->shard_len, kStepMaxBlocks);
+    const int64_t blocks = ((s->shard_len >> 3) + kStepVecPerBlock - 1) / kStepVecPerBlock;
     (void)hipGetLastError();
-    launch_step(a, grad_slices != nullptr, clip, blocks, static_cast<hipStream_t>(stream));
-    return launched();
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        a.v0 = b0 * kStepVecPerBlock;
+        rc = launch_step(a, grad_slices != nullptr, clip, nb, static_cast<hipStream_t>(stream));
+        if (rc != ZS_OK) return rc;
+    }
+    return ZS_OK;
 }
 
 extern "C" int shard_pack_gather(const zs_shard* s, const float* master, uint16_t* param_out,
@@ -589,9 +702,14 @@ extern "C" int shard_pack_gather(const zs_shard* s, const float* master, uint16_
     if (!param_out) return ZS_ENULL;
     if (s->valid_len > 0 && !master) return ZS_ENULL;
     if (!aligned16(param_out) || (master && !aligned16(master))) return ZS_EALIGN;
-    const int blocks = grid_for(s->valid_len, s->shard_len, kStepMaxBlocks);
+    const int64_t blocks = ((s->shard_len >> 3) + kStepThreads - 1) / kStepThreads;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                       master, slot_base(s, param_out), s->valid_len, s->shard_len);
-    return launched();
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        hipLaunchKernelGGL(k_pack, dim3(nb), dim3(kStepThreads), 0,
+                           static_cast<hipStream_t>(stream), master, slot_base(s, param_out),
+                           s->valid_len, s->shard_len, b0 * kStepThreads);
+        if ((rc = launched()) != ZS_OK) return rc;
+    }
+    return ZS_OK;
 }

@@ -177,5 +177,11 @@ def test_sqnorm_and_pack_error_paths():
 
 
 def test_workspace_is_modest():
-    s = Z.zs_layout(7_000_000_000, 8, 3, 1, 2)
-    assert 0 < Z.zs_workspace_bytes(s) <= 64 * 1024
+    # one fp64 partial per clip-pass block: at most 1/256 of the shard's
+    # fp32 mean, rounded up to 256 bytes
+    for psi, n_d, k in ((7_000_000_000, 8, 3), (70_000_000_000, 64, 0), (1, 4, 0),
+                        (1_048_576, 4, 1), (9, 2, 1)):
+        s = Z.zs_layout(psi, n_d, k, 1 if psi > 10**8 else 8, 2)
+        wsb = Z.zs_workspace_bytes(s)
+        assert 256 <= wsb <= max(256, s.valid_len * 4 // 256 + 256), (psi, wsb)
+        assert wsb % 256 == 0
