@@ -50,6 +50,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // The section 5 simulator's adamw evaluates 1 - beta and 1 - beta**t in
 // double; each scalar is computed in double and rounded to fp32 once.
+// A normal, positive power of two (its reciprocal is then exact).
+static bool is_pow2f(float x)
+{
+    if (!(x >= 1.17549435e-38f) || !std::isfinite(x)) return false;
+    int e = 0;
+    return std::frexp(x, &e) == 0.5f;
+}
+
 StepConsts make_consts(const zs_adamw* h)
 {
     const double t = static_cast<double>(h->step);
@@ -63,6 +71,10 @@ StepConsts make_consts(const zs_adamw* h)
     c.lr = static_cast<float>(h->lr);
     c.wd = static_cast<float>(h->weight_decay);
     c.eps = static_cast<float>(h->eps);
+    c.bc1_pow2 = is_pow2f(c.bc1) ? 1 : 0;
+    c.bc2_pow2 = is_pow2f(c.bc2) ? 1 : 0;
+    c.inv_bc1 = c.bc1_pow2 ? 1.0f / c.bc1 : 0.0f;
+    c.inv_bc2 = c.bc2_pow2 ? 1.0f / c.bc2 : 0.0f;
     return c;
 }
 
@@ -104,9 +116,11 @@ int zs_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align, int32_t sta
 
 size_t zs_workspace_bytes(const zs_shard* s)
 {
-    // One fp64 partial per clip-pass block, rounded up to 256 bytes.
+    // One fp64 partial per clip-pass block and one per group of them,
+    // rounded up to 256 bytes.
     const int64_t v = (s && s->valid_len > 0) ? s->valid_len : 0;
-    const int64_t bytes = zs::sq_blocks(v) * static_cast<int64_t>(sizeof(double));
+    const int64_t n = zs::sq_blocks(v);
+    const int64_t bytes = (n + zs::sq_groups(n)) * static_cast<int64_t>(sizeof(double));
     return static_cast<size_t>(zs::round_up(bytes > 0 ? bytes : 1, 256));
 }
 

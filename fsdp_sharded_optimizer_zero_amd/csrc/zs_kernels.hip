@@ -215,13 +215,14 @@ __device__ __forceinline__ float reduce_one(const Args& a, int64_t i)
 
 // ---- AdamW, one element ---------------------------------------------------------
 
+template <bool BC1_POW2 = false, bool BC2_POW2 = false>
 __device__ __forceinline__ void adamw1(const StepConsts& c, float g, float& w, float& m,
                                        float& v)
 {
     const float mi = (c.b1 * m) + (c.c1 * g);
     const float vi = (c.b2 * v) + ((c.c2 * g) * g);
-    const float mh = mi / c.bc1;
-    const float vh = vi / c.bc2;
+    const float mh = BC1_POW2 ? mi * c.inv_bc1 : mi / c.bc1;
+    const float vh = BC2_POW2 ? vi * c.inv_bc2 : vi / c.bc2;
     const float u = (mh / (sqrtf(vh) + c.eps)) + (c.wd * w);
     w = w - (c.lr * u);
     m = mi;
@@ -322,13 +323,27 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
     if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
 }
 
-// Clip pass 2: sum the n block partials in a fixed order (thread x takes
-// x, x + 1024, ... in order; then the block tree).
+// Clip pass 2: group g of block partials, [g*kSqGroup, (g+1)*kSqGroup), is
+// summed by block g (thread x takes x, x + 1024, ... in order; then the
+// block tree).
 __global__ void __launch_bounds__(kFinalThreads)
-    k_sqnorm_final(const double* partials, int64_t n, double* out, int accumulate)
+    k_sqnorm_groups(const double* partials, int64_t n, double* group_sums)
+{
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * kSqGroup;
+    const int64_t hi = lo + kSqGroup < n ? lo + kSqGroup : n;
+    double q = 0.0;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kFinalThreads) q = q + partials[i];
+    const double t = block_sum<kFinalThreads>(q);
+    if (threadIdx.x == 0) group_sums[blockIdx.x] = t;
+}
+
+// Clip pass 3: the n group sums, in the same fixed order; the result
+// replaces *out or is added to it.
+__global__ void __launch_bounds__(kFinalThreads)
+    k_sqnorm_final(const double* group_sums, int64_t n, double* out, int accumulate)
 {
     double q = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += kFinalThreads) q = q + partials[i];
+    for (int64_t i = threadIdx.x; i < n; i += kFinalThreads) q = q + group_sums[i];
     const double t = block_sum<kFinalThreads>(q);
     if (threadIdx.x == 0) *out = accumulate ? (*out + t) : t;
 }
@@ -350,17 +365,38 @@ __device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c,
     a.out[i] = static_cast<uint16_t>(bf16_rne(w));
 }
 
-// U full vectors at vi, vi + BS, ...: all loads, then the arithmetic, then
-// all stores.
+// AdamW on U vectors held in registers, bias corrections resolved.
+template <int U, bool CLIP, bool BC1_POW2, bool BC2_POW2>
+__device__ __forceinline__ void adamw_vectors(const StepConsts& c, float coef,
+                                              const float (&g)[U][8], float (&W)[U][8],
+                                              float (&M)[U][8], float (&V)[U][8])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float gj = g[u][j];
+            if constexpr (CLIP) gj = gj * coef;
+            adamw1<BC1_POW2, BC2_POW2>(c, gj, W[u][j], M[u][j], V[u][j]);
+        }
+    }
+}
+
+// U full vectors at vi, vi + BS, ...: all loads, then the clip coefficient
+// and the arithmetic, then all stores.  The scheduling barrier keeps every
+// load ahead of any arithmetic, so a wave waits for memory once and
+// computes the fp64 clip coefficient while its loads are in flight.  A
+// uniform branch then picks the arithmetic for this step's bias
+// corrections.
 template <int U, int BS, bool FROM_SLICES, int NDT, bool CLIP>
-__device__ __forceinline__ void step_vectors(const StepArgs& a, const StepConsts& c, float coef,
-                                             int64_t vi)
+__device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
 {
     f32x4* w4 = reinterpret_cast<f32x4*>(a.w);
     f32x4* m4 = reinterpret_cast<f32x4*>(a.m);
     f32x4* v4 = reinterpret_cast<f32x4*>(a.v);
     u32x4* o4 = reinterpret_cast<u32x4*>(a.out);
-    float g[U][8], W[U][8], M[U][8], V[U][8];
+    float g[U][8];
+    f32x4 w0[U], w1[U], m0[U], m1[U], v0[U], v1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t x = vi + u * BS;
@@ -372,24 +408,31 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, const StepConsts
             g[u][0] = x0.x; g[u][1] = x0.y; g[u][2] = x0.z; g[u][3] = x0.w;
             g[u][4] = x1.x; g[u][5] = x1.y; g[u][6] = x1.z; g[u][7] = x1.w;
         }
-        const f32x4 w0 = w4[2 * x], w1 = w4[2 * x + 1];
-        const f32x4 m0 = m4[2 * x], m1 = m4[2 * x + 1];
-        const f32x4 v0 = v4[2 * x], v1 = v4[2 * x + 1];
-        W[u][0] = w0.x; W[u][1] = w0.y; W[u][2] = w0.z; W[u][3] = w0.w;
-        W[u][4] = w1.x; W[u][5] = w1.y; W[u][6] = w1.z; W[u][7] = w1.w;
-        M[u][0] = m0.x; M[u][1] = m0.y; M[u][2] = m0.z; M[u][3] = m0.w;
-        M[u][4] = m1.x; M[u][5] = m1.y; M[u][6] = m1.z; M[u][7] = m1.w;
-        V[u][0] = v0.x; V[u][1] = v0.y; V[u][2] = v0.z; V[u][3] = v0.w;
-        V[u][4] = v1.x; V[u][5] = v1.y; V[u][6] = v1.z; V[u][7] = v1.w;
+        w0[u] = w4[2 * x]; w1[u] = w4[2 * x + 1];
+        m0[u] = m4[2 * x]; m1[u] = m4[2 * x + 1];
+        v0[u] = v4[2 * x]; v1[u] = v4[2 * x + 1];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    float coef = 1.0f;
+    if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
+    __builtin_amdgcn_sched_barrier(0);
+    const StepConsts c = a.c;
+    float W[U][8], M[U][8], V[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float gj = g[u][j];
-            if constexpr (CLIP) gj = gj * coef;
-            adamw1(c, gj, W[u][j], M[u][j], V[u][j]);
-        }
+        W[u][0] = w0[u].x; W[u][1] = w0[u].y; W[u][2] = w0[u].z; W[u][3] = w0[u].w;
+        W[u][4] = w1[u].x; W[u][5] = w1[u].y; W[u][6] = w1[u].z; W[u][7] = w1[u].w;
+        M[u][0] = m0[u].x; M[u][1] = m0[u].y; M[u][2] = m0[u].z; M[u][3] = m0[u].w;
+        M[u][4] = m1[u].x; M[u][5] = m1[u].y; M[u][6] = m1[u].z; M[u][7] = m1[u].w;
+        V[u][0] = v0[u].x; V[u][1] = v0[u].y; V[u][2] = v0[u].z; V[u][3] = v0[u].w;
+        V[u][4] = v1[u].x; V[u][5] = v1[u].y; V[u][6] = v1[u].z; V[u][7] = v1[u].w;
+    }
+    if (c.bc1_pow2) {
+        if (c.bc2_pow2) adamw_vectors<U, CLIP, true, true>(c, coef, g, W, M, V);
+        else adamw_vectors<U, CLIP, true, false>(c, coef, g, W, M, V);
+    } else {
+        if (c.bc2_pow2) adamw_vectors<U, CLIP, false, true>(c, coef, g, W, M, V);
+        else adamw_vectors<U, CLIP, false, false>(c, coef, g, W, M, V);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -414,24 +457,25 @@ template <bool FROM_SLICES, int NDT, bool CLIP>
 __global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
 {
     constexpr int BS = kStepThreads, U = kStepU;
-    float coef = 1.0f;
-    if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
-    const StepConsts c = a.c;
     const int64_t nfull = a.valid_len >> 3;
     const int64_t nslot = a.shard_len >> 3;
     const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kStepVecPerBlock;
     if (base + kStepVecPerBlock <= nfull) {
-        step_vectors<U, BS, FROM_SLICES, NDT, CLIP>(a, c, coef, base + threadIdx.x);
+        step_vectors<U, BS, FROM_SLICES, NDT, CLIP>(a, base + threadIdx.x);
         return;
     }
     for (int u = 0; u < U; ++u) {
         const int64_t vi = base + u * BS + threadIdx.x;
         if (vi < nfull) {
-            step_vectors<1, BS, FROM_SLICES, NDT, CLIP>(a, c, coef, vi);
+            step_vectors<1, BS, FROM_SLICES, NDT, CLIP>(a, vi);
         } else if (vi < nslot) {
             // The partial vector (its valid elements), then pads.
             int64_t i = vi * 8;
-            for (; i < a.valid_len; ++i) step_one<FROM_SLICES, NDT, CLIP>(a, c, coef, i);
+            if (i < a.valid_len) {
+                float coef = 1.0f;
+                if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
+                for (; i < a.valid_len; ++i) step_one<FROM_SLICES, NDT, CLIP>(a, a.c, coef, i);
+            }
             if (i == vi * 8) {
                 reinterpret_cast<u32x4*>(a.out)[vi] = u32x4{0u, 0u, 0u, 0u};
             } else {
@@ -633,8 +677,15 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
         a.partials = partials + b0;
         if ((rc = launch_sqnorm(a, mean_out != nullptr, nb, st)) != ZS_OK) return rc;
     }
+    const int64_t groups = sq_groups(blocks);
+    double* group_sums = partials + blocks;
+    if (groups > 0) {
+        hipLaunchKernelGGL(k_sqnorm_groups, dim3(groups), dim3(kFinalThreads), 0, st,
+                           static_cast<const double*>(partials), blocks, group_sums);
+        if ((rc = launched()) != ZS_OK) return rc;
+    }
     hipLaunchKernelGGL(k_sqnorm_final, dim3(1), dim3(kFinalThreads), 0, st,
-                       static_cast<const double*>(partials), blocks, sqnorm_out,
+                       static_cast<const double*>(group_sums), groups, sqnorm_out,
                        accumulate ? 1 : 0);
     return launched();
 }

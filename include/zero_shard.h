@@ -114,9 +114,9 @@ int zs_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align, int32_t sta
               int32_t out_mode, zs_shard* out);
 
 /* Bytes of device workspace shard_grad_sqnorm needs: one fp64 partial sum
- * per block of its first pass (one block per 4096 parameters), rounded up
- * to 256 bytes -- 1.7 MB for an 875M-parameter shard, at least 256 bytes
- * (an empty shard).  Host only. */
+ * per block of its first pass (one block per 4096 parameters) plus one per
+ * group of 4096 such partials, rounded up to 256 bytes -- 1.7 MB for an
+ * 875M-parameter shard, at least 256 bytes (an empty shard).  Host only. */
 size_t zs_workspace_bytes(const zs_shard* s);
 
 /* Model-state bytes per GPU of the Theorem's table: weights and gradients
