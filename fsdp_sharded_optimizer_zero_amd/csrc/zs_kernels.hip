@@ -51,16 +51,21 @@ namespace {
 // Blocks of the step / of the clip pass that may be resident on one CU at
 // a time (0: no cap).  A dynamic LDS reservation enforces the cap.  Few
 // resident waves keep the window of addresses in flight narrow, which suits
-// the HBM better than a full CU when 4 to 9 arrays stream at once.  Measured
-// on MI355X over an 875M-parameter shard: the step is ~7% faster at two
-// 256-thread blocks per CU than uncapped (one block leaves its division and
-// square-root chain exposed), the clip pass ~4% faster at one 512-thread
-// block per CU.
+// the HBM better than a full CU when 4 to 65 arrays stream at once.
+// Measured on MI355X: the step over an 875M-parameter shard is ~7% faster
+// at two 256-thread blocks per CU than uncapped (one block leaves its
+// division and square-root chain exposed); the clip pass is fastest at two
+// 512-thread blocks per CU over 8 slices and at one over 64.
 #ifndef ZS_STEP_PER_CU
 #define ZS_STEP_PER_CU 2
 #endif
 #ifndef ZS_SQ_PER_CU
-#define ZS_SQ_PER_CU 1
+#define ZS_SQ_PER_CU 2
+#endif
+// The clip pass with this many slices or more keeps enough loads in flight
+// per thread to run at one block per CU.
+#ifndef ZS_SQ_WIDE_ND
+#define ZS_SQ_WIDE_ND 32
 #endif
 // Non-temporal (streaming) cache policy: stores of the step; loads and
 // stores of the clip pass.  Every byte here is touched once per pass.
@@ -72,6 +77,10 @@ namespace {
 #endif
 #ifndef ZS_SQ_NT_STORE
 #define ZS_SQ_NT_STORE 1
+#endif
+// Gradient slices whose loads one thread has in flight at once.
+#ifndef ZS_RED_GROUP
+#define ZS_RED_GROUP 8
 #endif
 constexpr int kStepThreads = ZS_STEP_BS;
 constexpr int kStepU = ZS_STEP_U;
@@ -100,6 +109,36 @@ __device__ __forceinline__ void store(T* p, T v)
 {
     if constexpr (NT) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+// Non-temporal 16-byte store of four floats, issued as an integer vector:
+// the optimizer rebuilds float-vector stores from their scalar lanes and
+// drops the non-temporal hint on the way.
+template <bool NT>
+__device__ __forceinline__ void store_f4(f32x4* p, f32x4 v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// A buffer resource over `bytes` bytes from `base` (uniform across the
+// wave), for 16-byte stores at per-lane byte offsets with an explicit cache
+// policy.  The generic non-temporal hint is lost by the optimizer on some
+// float-vector stores; the buffer store keeps it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, uint32_t bytes)
+{
+    // dword 3: 32-bit data format, as CDNA raw buffer accesses require
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+
+constexpr int kCachePolicyNt = 2;   // the instruction's nt bit
+
+template <bool NT>
+__device__ __forceinline__ void buffer_store_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v)
+{
+    const u32x4 b = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                     __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, NT ? kCachePolicyNt : 0);
 }
 
 struct SlicePtrs {
@@ -187,9 +226,9 @@ __device__ __forceinline__ void reduce_vec(const Args& a, int64_t vi, float g[8]
     g[2] = bf16_lo(x.y); g[3] = bf16_hi(x.y);
     g[4] = bf16_lo(x.z); g[5] = bf16_hi(x.z);
     g[6] = bf16_lo(x.w); g[7] = bf16_hi(x.w);
-    // Loads are issued 8 ranks at a time (bounded registers), the additions
-    // stay in rank order.
-    constexpr int G = 8;
+    // Loads are issued ZS_RED_GROUP ranks at a time (bounded registers), the
+    // additions stay in rank order.
+    constexpr int G = ZS_RED_GROUP;
     for (int r0 = 1; r0 < nd; r0 += G) {
         u32x4 b[G];
 #pragma unroll
@@ -238,6 +277,11 @@ __device__ __forceinline__ float clip_coef(double Q, double max_norm)
     return static_cast<float>(c);
 }
 
+// q + d*d for d widened from fp32: d*d has at most 48 significant bits, so
+// it is exact in fp64 and one fused multiply-add rounds exactly as the
+// multiply followed by the add.
+__device__ __forceinline__ double sq_add(double q, double d) { return __builtin_fma(d, d, q); }
+
 // ---- deterministic fp64 block sum (result valid in thread 0) ------------------
 
 template <int BS>
@@ -279,18 +323,22 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
         float g[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u) reduce_vec<NDT, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
+        // The block's kSqVecPerBlock * 32 bytes of the mean (unused when
+        // the mean is not stored: then mean_out is null and nothing is
+        // written through it).
+        const __amdgpu_buffer_rsrc_t mr =
+            buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t vi = base + u * BS + threadIdx.x;
             if constexpr (STORE) {
-                f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
-                store<kSqNtStore>(o, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
-                store<kSqNtStore>(o + 1, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
+                const uint32_t off = static_cast<uint32_t>((u * BS + threadIdx.x) * 32);
+                buffer_store_f4<kSqNtStore>(mr, off, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
+                buffer_store_f4<kSqNtStore>(mr, off + 16, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const double d = g[u][j];
-                q = q + d * d;
+                q = sq_add(q, d);
             }
         }
     } else {
@@ -301,20 +349,20 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
                 reduce_vec<NDT, kSqNtLoad>(a, vi, g);
                 if constexpr (STORE) {
                     f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
-                    store<kSqNtStore>(o, f32x4{g[0], g[1], g[2], g[3]});
-                    store<kSqNtStore>(o + 1, f32x4{g[4], g[5], g[6], g[7]});
+                    store_f4<kSqNtStore>(o, f32x4{g[0], g[1], g[2], g[3]});
+                    store_f4<kSqNtStore>(o + 1, f32x4{g[4], g[5], g[6], g[7]});
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const double d = g[j];
-                    q = q + d * d;
+                    q = sq_add(q, d);
                 }
             } else if (vi == nfull) {
                 for (int64_t i = vi * 8; i < a.valid_len; ++i) {
                     const float g = reduce_one<NDT>(a, i);
                     if constexpr (STORE) a.mean_out[i] = g;
                     const double d = g;
-                    q = q + d * d;
+                    q = sq_add(q, d);
                 }
             }
         }
@@ -438,12 +486,12 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
     for (int u = 0; u < U; ++u) {
         const int64_t x = vi + u * BS;
         constexpr bool NT = kStepNtStore;
-        store<NT>(w4 + 2 * x, f32x4{W[u][0], W[u][1], W[u][2], W[u][3]});
-        store<NT>(w4 + 2 * x + 1, f32x4{W[u][4], W[u][5], W[u][6], W[u][7]});
-        store<NT>(m4 + 2 * x, f32x4{M[u][0], M[u][1], M[u][2], M[u][3]});
-        store<NT>(m4 + 2 * x + 1, f32x4{M[u][4], M[u][5], M[u][6], M[u][7]});
-        store<NT>(v4 + 2 * x, f32x4{V[u][0], V[u][1], V[u][2], V[u][3]});
-        store<NT>(v4 + 2 * x + 1, f32x4{V[u][4], V[u][5], V[u][6], V[u][7]});
+        store_f4<NT>(w4 + 2 * x, f32x4{W[u][0], W[u][1], W[u][2], W[u][3]});
+        store_f4<NT>(w4 + 2 * x + 1, f32x4{W[u][4], W[u][5], W[u][6], W[u][7]});
+        store_f4<NT>(m4 + 2 * x, f32x4{M[u][0], M[u][1], M[u][2], M[u][3]});
+        store_f4<NT>(m4 + 2 * x + 1, f32x4{M[u][4], M[u][5], M[u][6], M[u][7]});
+        store_f4<NT>(v4 + 2 * x, f32x4{V[u][0], V[u][1], V[u][2], V[u][3]});
+        store_f4<NT>(v4 + 2 * x + 1, f32x4{V[u][4], V[u][5], V[u][6], V[u][7]});
         store<NT>(o4 + x, u32x4{pack_bf16x2(W[u][0], W[u][1]), pack_bf16x2(W[u][2], W[u][3]),
                                 pack_bf16x2(W[u][4], W[u][5]), pack_bf16x2(W[u][6], W[u][7])});
     }
@@ -562,7 +610,8 @@ template <int NDT, bool STORE>
 int launch_sqnorm_k(const SqArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
-    const int rc = lds_reservation<k_reduce_sqnorm<NDT, STORE>>(ZS_SQ_PER_CU, &lds);
+    const int per_cu = a.n_d >= ZS_SQ_WIDE_ND ? 1 : ZS_SQ_PER_CU;
+    const int rc = lds_reservation<k_reduce_sqnorm<NDT, STORE>>(per_cu, &lds);
     if (rc != ZS_OK) return rc;
     hipLaunchKernelGGL((k_reduce_sqnorm<NDT, STORE>), dim3(blocks), dim3(kSqThreads), lds, st, a);
     return launched();
