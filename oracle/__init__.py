@@ -102,6 +102,14 @@ def lib():
         L.or_bf16_rne_array.restype = None
         L.or_reduce_mean.argtypes = [i32, C.c_void_p, i64, C.c_void_p]
         L.or_reduce_mean.restype = None
+        L.or_reduce_mean_f32in.argtypes = [i32, C.c_void_p, i64, C.c_void_p]
+        L.or_reduce_mean_f32in.restype = None
+        L.or_token_weights.argtypes = [i32, C.c_void_p, C.c_void_p]
+        L.or_token_weights.restype = C.c_int
+        L.or_reduce_weighted.argtypes = [i32, i32, C.c_void_p, C.c_void_p, i64, C.c_void_p]
+        L.or_reduce_weighted.restype = None
+        L.or_accumulate.argtypes = [i64, C.c_void_p, i32, i32, C.c_void_p]
+        L.or_accumulate.restype = None
         L.or_sqacc_size.argtypes = []
         L.or_sqacc_size.restype = i64
         L.or_sqacc_init.argtypes = [C.c_void_p]
@@ -210,6 +218,58 @@ def reduce_mean(slices) -> np.ndarray:
     lib().or_reduce_mean(len(slices), _ptr_array(slices, np.uint16), n,
                          _ptr(out, np.float32))
     return out
+
+
+def reduce_mean_f32(slices) -> np.ndarray:
+    """Rank-order mean of fp32 slices (the fp32 reduce_dtype reading)."""
+    n = slices[0].size
+    for sl in slices:
+        if sl.size != n:
+            raise ValueError("slices must have equal length")
+    out = np.empty(n, dtype=np.float32)
+    lib().or_reduce_mean_f32in(len(slices), _ptr_array(slices, np.float32), n,
+                               _ptr(out, np.float32))
+    return out
+
+
+class ZeroTokens(ValueError):
+    """The global valid-token count is zero: every rank rejects the update."""
+
+
+def token_weights(tokens) -> np.ndarray:
+    t = np.ascontiguousarray(tokens, dtype=np.int64)
+    w = np.empty(t.size, dtype=np.float32)
+    rc = lib().or_token_weights(t.size, _ptr(t, np.int64), _ptr(w, np.float32))
+    if rc == -2:
+        raise ZeroTokens("global token count is zero")
+    if rc != 0:
+        raise ValueError(f"invalid token counts ({rc})")
+    return w
+
+
+def reduce_weighted(slices, w) -> np.ndarray:
+    """Token-weighted rank-order sum of bf16 (uint16) or fp32 slices."""
+    n = slices[0].size
+    f32in = slices[0].dtype == np.float32
+    dt = np.float32 if f32in else np.uint16
+    for sl in slices:
+        if sl.size != n:
+            raise ValueError("slices must have equal length")
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.size != len(slices):
+        raise ValueError("one weight per slice")
+    out = np.empty(n, dtype=np.float32)
+    lib().or_reduce_weighted(len(slices), 1 if f32in else 0, _ptr_array(slices, dt),
+                             _ptr(w, np.float32), n, _ptr(out, np.float32))
+    return out
+
+
+def accumulate(r_j: np.ndarray, j: int, m: int, acc: np.ndarray) -> None:
+    """Micro-batch j of m into the fp32 accumulator (in place); after the
+    last one acc holds the step's gradient, the mean over micro-batches."""
+    if r_j.size != acc.size or not (0 <= j < m):
+        raise ValueError("bad accumulate call")
+    lib().or_accumulate(acc.size, _ptr(r_j, np.float32), j, m, _ptr(acc, np.float32))
 
 
 def sqnorm(g: np.ndarray) -> float:

@@ -145,6 +145,60 @@ void or_reduce_mean(int32_t n_d, const uint16_t* const* slices, int64_t n,
     }
 }
 
+void or_reduce_mean_f32in(int32_t n_d, const float* const* slices, int64_t n,
+                          float* g_out)
+{
+    const float ranks = (float)n_d;
+    for (int64_t i = 0; i < n; ++i) {
+        float sum = slices[0][i];
+        for (int32_t r = 1; r < n_d; ++r)
+            sum = sum + slices[r][i];
+        g_out[i] = sum / ranks;
+    }
+}
+
+int or_token_weights(int32_t n_d, const int64_t* tokens, float* w_out)
+{
+    double T = 0.0;
+    for (int32_t r = 0; r < n_d; ++r) {
+        if (tokens[r] < 0) return -1;
+        T += (double)tokens[r];
+    }
+    if (T == 0.0) return -2;
+    for (int32_t r = 0; r < n_d; ++r) w_out[r] = (float)((double)tokens[r] / T);
+    return 0;
+}
+
+static float slice_value(int32_t f32in, const void* slice, int64_t i)
+{
+    if (f32in) return ((const float*)slice)[i];
+    return or_bf16_to_f32(((const uint16_t*)slice)[i]);
+}
+
+void or_reduce_weighted(int32_t n_d, int32_t f32in, const void* const* slices,
+                        const float* w, int64_t n, float* g_out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float s = w[0] * slice_value(f32in, slices[0], i);
+        for (int32_t r = 1; r < n_d; ++r) {
+            const float p = w[r] * slice_value(f32in, slices[r], i);
+            s = s + p;
+        }
+        g_out[i] = s;
+    }
+}
+
+void or_accumulate(int64_t n, const float* r_j, int32_t j, int32_t m,
+                   float* acc)
+{
+    const float mf = (float)m;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = (j == 0) ? r_j[i] : acc[i] + r_j[i];
+        if (j == m - 1 && m > 1) a = a / mf;
+        acc[i] = a;
+    }
+}
+
 /* ---- O2 / O3 -------------------------------------------------------------- */
 
 void or_sqacc_init(or_sqacc* a)

@@ -99,6 +99,48 @@ void     or_bf16_rne_array(const float* x, int64_t n, uint16_t* out);
 void or_reduce_mean(int32_t n_d, const uint16_t* const* slices, int64_t n,
                     float* g_out);
 
+/* ---- reductions beyond the bf16 mean --------------------------------------- */
+/* fp32 gradient slices.  [DPZ] "tokens that hide the all-reduce" (fp32
+ * gradient reduction doubles the bytes) and §6 "Where it shows up" (Llama 3
+ * reduce-scattered gradients in fp32); [DDB] "FSDP1 and FSDP2: explicitly
+ * different versioned paths", its mixed-precision policy
+ * reduce_dtype=torch.float32.  Reading: the rank-order fp32 sum of
+ * or_reduce_mean, from fp32 inputs, divided by (float)n_d once. */
+void or_reduce_mean_f32in(int32_t n_d, const float* const* slices, int64_t n,
+                          float* g_out);
+
+/* Token-weighted reduction.  [DPZ] §7 "Common mistakes": with a per-token
+ * loss and a different number of tokens on each GPU, weight each GPU's
+ * gradient by its token count.  [DDB] "DDP: replicated state, partitioned
+ * examples": ranks with 2 and 6 tokens and local mean losses 3 and 1 give
+ * (2*3+6*1)/8 = 1.5, not 2; a zero-token rank contributes a zero and still
+ * takes part; [DDB] "Practice and worked answers", item 4: if the global
+ * count is zero every rank rejects the update.
+ * Reading: slice r holds the gradient of rank r's local mean loss;
+ * w_r = f32(n_r / T), T = sum of n_r, in double; then
+ * g = (((w_0*G_0) + (w_1*G_1)) + ...) in rank order, every product and every
+ * sum rounded to fp32.  or_token_weights returns 0, -1 if a count is
+ * negative, -2 if T == 0 (the update is rejected; w_out untouched).
+ * f32in: 0 -> slices are bf16 (uint16_t), 1 -> fp32. */
+int  or_token_weights(int32_t n_d, const int64_t* tokens, float* w_out);
+void or_reduce_weighted(int32_t n_d, int32_t f32in, const void* const* slices,
+                        const float* w, int64_t n, float* g_out);
+
+/* ZeRO-2 gradient accumulation.  [DPZ] §3 "Gradient accumulation": m
+ * micro-batches run one after the other and their gradients are added
+ * before one optimizer step; ZeRO-2 keeps no full gradient, so it
+ * reduce-scatters after every micro-batch (table row ZeRO-2).  [DDB]
+ * "Accumulation, clipping and scaling measurements": clipping and the
+ * optimizer act at the effective-update boundary, after the last
+ * micro-batch.  Reading:
+ * micro-batch j's reduced slice r_j (any reduction above) is added in fp32
+ * into a persistent shard accumulator in micro-batch order: acc = r_0, then
+ * acc = acc + r_j; after the last one (j = m-1) the step's gradient is
+ * acc / (float)m, correctly rounded: the mean over the m micro-batches.
+ * For m == 1, acc = r_0. */
+void or_accumulate(int64_t n, const float* r_j, int32_t j, int32_t m,
+                   float* acc);
+
 /* ---- O2/O3: global gradient-norm clip ------------------------------------ */
 /* [DPZ] §7 "Common mistakes", last item: with sharded gradients the global
  * norm is an all-reduce of the squared shard norms.  [DDB] reference DDP

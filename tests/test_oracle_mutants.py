@@ -63,6 +63,23 @@ MUTANTS = {
     "f64_drops_weight_decay": [("(mh / (sqrt(vh) + h->eps) + h->weight_decay * w[i])",
                                 "(mh / (sqrt(vh) + h->eps))")],
     "f64_mean_is_sum": [("g_out[i] = s / (double)n_d;", "g_out[i] = s;")],
+    "f32in_wrong_rank_index": [("sum = sum + slices[r][i];", "sum = sum + slices[0][i];")],
+    "f32in_sum_not_mean": [("g_out[i] = sum / ranks;", "g_out[i] = sum;")],
+    "f32in_reverse_order": [("float sum = slices[0][i];", "float sum = slices[n_d - 1][i];"),
+                            ("sum = sum + slices[r][i];", "sum = sum + slices[n_d - 1 - r][i];")],
+    "token_weight_float_division": [("w_out[r] = (float)((double)tokens[r] / T);",
+                                     "w_out[r] = (float)tokens[r] / (float)T;")],
+    "token_zero_total_accepted": [("if (T == 0.0) return -2;", "")],
+    "token_negative_accepted": [("if (tokens[r] < 0) return -1;", "")],
+    "weighted_drops_first_weight": [("float s = w[0] * slice_value(f32in, slices[0], i);",
+                                     "float s = slice_value(f32in, slices[0], i);")],
+    "weighted_wrong_weight_index": [("const float p = w[r] * slice_value(f32in, slices[r], i);",
+                                     "const float p = w[0] * slice_value(f32in, slices[r], i);")],
+    "accumulate_sum_not_mean": [("if (j == m - 1 && m > 1) a = a / mf;", "")],
+    "accumulate_reads_acc_first": [("float a = (j == 0) ? r_j[i] : acc[i] + r_j[i];",
+                                    "float a = acc[i] + r_j[i];")],
+    "accumulate_divides_every_step": [("if (j == m - 1 && m > 1) a = a / mf;",
+                                       "if (m > 1) a = a / mf;")],
 }
 
 

@@ -644,3 +644,156 @@ def test_shard_step_against_torch_clip_and_adamw(n_d, max_norm):
              .view(np.uint16).astype(np.int32))
     assert np.all(np.abs(out[:V].astype(np.int32) - ref16) <= 1)
     assert not out[V:].any()
+
+
+# ------------------------------------------------- fp32 gradient slices (reduce_dtype)
+
+def test_reduce_f32_worked_example():
+    """The worked example with fp32 slices: -1.5 and -13 (two ranks), and the
+    four per-sample gradients (four ranks), average to -7.25."""
+    g = golden("worked_example_two_gpus.json")
+    two = O.reduce_mean_f32([np.array([m], np.float32) for m in g["gpu_means"]])
+    four = O.reduce_mean_f32([np.array([v], np.float32) for v in g["grad_per_sample"]])
+    assert two[0] == np.float32(g["allreduce_mean"])
+    assert four[0] == np.float32(g["allreduce_mean"])
+
+
+def test_reduce_f32_equals_bf16_path_on_bf16_values():
+    """fp32 slices holding bf16 values (the FSDP2 bf16-param / fp32-reduce
+    policy widens bf16 gradients) give the bf16 reduction's bits."""
+    rng = np.random.default_rng(21)
+    for n_d in (1, 2, 3, 5, 8, 64):
+        sl = [O.bf16_rne(rng.normal(0, 1e-3, 777).astype(np.float32)) for _ in range(n_d)]
+        a = O.reduce_mean(sl)
+        b = O.reduce_mean_f32([O.bf16_to_f32(x).copy() for x in sl])
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_reduce_f32_exact_and_correctly_rounded():
+    """Sums of these dyadic values are exact in fp32, so the result is the
+    exact mean rounded once (any N_d, power of two or not)."""
+    rng = np.random.default_rng(22)
+    for n_d in (1, 2, 3, 4, 7, 8, 64):
+        ints = rng.integers(-(1 << 16), 1 << 16, size=(n_d, 129))
+        sl = [np.ascontiguousarray((r * 2.0 ** -30).astype(np.float32)) for r in ints]
+        got = O.reduce_mean_f32(sl)
+        for i in range(129):
+            exact = Fraction(int(ints[:, i].sum()), 1 << 30) / n_d
+            assert got[i] == np.float32(float(exact))
+
+
+def test_reduce_f32_rank_order():
+    """1 + 2^-24 is a tie that rounds to 1, twice; the reverse order would
+    give 1 + 2^-23 exactly."""
+    sl = [np.array([1.0], np.float32), np.array([2.0 ** -24], np.float32),
+          np.array([2.0 ** -24], np.float32)]
+    got = O.reduce_mean_f32(sl)[0]
+    assert got == np.float32(1.0) / np.float32(3.0)
+    assert got != np.float32(1.0 + 2.0 ** -23) / np.float32(3.0)
+
+
+# ------------------------------------------------------- token-weighted reduction
+
+def test_token_weights_worked_example():
+    """Two ranks with 2 and 6 valid tokens and local mean losses 3 and 1: the
+    global mean is (2*3 + 6*1)/8 = 1.5, not the plain average 2."""
+    w = O.token_weights([2, 6])
+    assert w.tolist() == [0.25, 0.75]
+    for sl in ([np.array([3.0], np.float32), np.array([1.0], np.float32)],
+               [bf16_of_exact([3.0]), bf16_of_exact([1.0])]):
+        assert O.reduce_weighted(sl, w)[0] == np.float32(1.5)
+    assert O.reduce_mean([bf16_of_exact([3.0]), bf16_of_exact([1.0])])[0] == np.float32(2.0)
+
+
+def test_token_weights_zero_token_rank_and_zero_total():
+    """A zero-token rank contributes zero: the result is the other ranks'
+    weighted sum exactly; a zero global count rejects the update."""
+    rng = np.random.default_rng(23)
+    g1 = rng.normal(0, 1e-3, 1000).astype(np.float32)
+    g0 = rng.normal(0, 1e-3, 1000).astype(np.float32)
+    got = O.reduce_weighted([g0, g1], O.token_weights([0, 17]))
+    assert np.array_equal(got.view(np.uint32), g1.view(np.uint32))
+    with pytest.raises(O.ZeroTokens):
+        O.token_weights([0, 0, 0])
+    with pytest.raises(ValueError):
+        O.token_weights([3, -1])
+
+
+def test_token_weights_rounded_once_from_double():
+    """w_r = f32(n_r / T) computed in double: 16777217 is not an fp32 value,
+    so dividing the fp32-rounded counts would give another weight."""
+    w = O.token_weights([16777217, 1])
+    T = 16777218
+    assert w[0] == np.float32(16777217 / T) and w[1] == np.float32(1 / T)
+    assert w[0] != np.float32(16777217) / np.float32(T)
+
+
+def test_token_weights_equal_counts_is_the_mean():
+    """Equal counts over a power-of-two number of ranks: w_r = 2^-k exactly,
+    and scaling by 2^-k commutes with rounding, so the weighted sum is the
+    plain mean bit for bit (normal values)."""
+    rng = np.random.default_rng(24)
+    for n_d in (1, 2, 4, 8, 64):
+        sl = [O.bf16_rne(rng.normal(0, 1e-3, 513).astype(np.float32)) for _ in range(n_d)]
+        got = O.reduce_weighted(sl, O.token_weights([4096] * n_d))
+        assert np.array_equal(got.view(np.uint32), O.reduce_mean(sl).view(np.uint32))
+
+
+def test_token_weighted_exact_on_dyadics():
+    rng = np.random.default_rng(25)
+    tokens = [1, 3, 0, 4]            # T = 8: weights 1/8, 3/8, 0, 4/8 exact
+    w = O.token_weights(tokens)
+    ints = rng.integers(-255, 256, size=(4, 200))
+    sl = [bf16_of_exact(r * 2.0 ** -12) for r in ints]
+    got = O.reduce_weighted(sl, w)
+    for i in range(200):
+        exact = sum(Fraction(tokens[r], 8) * Fraction(int(ints[r, i]), 1 << 12) for r in range(4))
+        assert Fraction(float(got[i])) == exact
+
+
+# ------------------------------------------------- ZeRO-2 gradient accumulation
+
+def test_accumulate_worked_example():
+    """Gradient accumulation on one rank: micro-batches [x1, x2] and [x3, x4]
+    have mean gradients -1.5 and -13; accumulating both and taking the mean
+    over micro-batches gives -7.25, the full-batch gradient."""
+    g = golden("worked_example_two_gpus.json")
+    acc = np.full(1, np.nan, np.float32)      # never read on the first micro-batch
+    for j, mj in enumerate(g["gpu_means"]):
+        O.accumulate(np.array([mj], np.float32), j, 2, acc)
+    assert acc[0] == np.float32(g["one_gpu_full_batch_mean"])
+
+
+def test_accumulate_single_micro_batch_is_identity():
+    rng = np.random.default_rng(26)
+    r = rng.normal(0, 1.0, 300).astype(np.float32)
+    acc = np.full(300, np.nan, np.float32)
+    O.accumulate(r, 0, 1, acc)
+    assert np.array_equal(acc.view(np.uint32), r.view(np.uint32))
+
+
+def test_accumulate_zero2_equals_ddp_accumulation_on_dyadics():
+    """ZeRO-2 reduces every micro-batch and adds the reduced slices; DDP
+    (no_sync) adds full local gradients and reduces once.  On values whose
+    sums are exact both equal the mean over all m * N_d contributions."""
+    rng = np.random.default_rng(27)
+    for n_d, m in ((1, 4), (2, 2), (4, 3), (8, 4)):
+        ints = rng.integers(-255, 256, size=(m, n_d, 65))
+        acc = np.empty(65, np.float32)
+        for j in range(m):
+            r_j = O.reduce_mean([bf16_of_exact(ints[j, r] * 2.0 ** -8) for r in range(n_d)])
+            O.accumulate(r_j, j, m, acc)
+        for i in range(65):
+            exact = Fraction(int(ints[:, :, i].sum()), 256 * n_d * m)
+            if m & (m - 1) == 0:
+                assert Fraction(float(acc[i])) == exact
+            else:                                   # one rounding, by 1/m
+                assert acc[i] == np.float32(float(exact))
+
+
+def test_accumulate_micro_batch_order():
+    """((2^24 + 1) + 1) / 3 in micro-batch order rounds to 2^24 / 3."""
+    acc = np.empty(1, np.float32)
+    for j, v in enumerate((2.0 ** 24, 1.0, 1.0)):
+        O.accumulate(np.array([v], np.float32), j, 3, acc)
+    assert acc[0] == np.float32(2.0 ** 24) / np.float32(3.0)
