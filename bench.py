@@ -56,7 +56,7 @@ def cpu_baseline(wl, shard, seconds: float):
     import oracle as O
     import zsgen
     from zsgen.workloads import (STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_MASTER,
-                                 grad_stream)
+                                 grad_key, grad_stream)
 
     h = O.Hparams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
                   weight_decay=wl.weight_decay, step=wl.t0, max_grad_norm=wl.max_grad_norm)
@@ -64,11 +64,26 @@ def cpu_baseline(wl, shard, seconds: float):
     done, spent = 0, 0.0
     acc = O.SqAcc()
     off, V = shard.shard_offset, shard.valid_len
+    m_count = wl.micro_batches
+    weights = O.token_weights(wl.rank_tokens) if wl.rank_tokens else None
+
+    def slices(j, n):
+        key = grad_key(wl.t0, j, m_count)
+        if wl.grad_dtype == "f32":
+            return [zsgen.host_f32(wl.seed, grad_stream(0), r, key, wl.grad_sigma, off + done, n)
+                    for r in range(wl.n_d)]
+        return [zsgen.host_bf16(wl.seed, grad_stream(0), r, key, wl.grad_sigma, off + done, n,
+                                p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
+                for r in range(wl.n_d)]
+
+    def reduce(sl):
+        if weights is not None:
+            return O.reduce_weighted(sl, weights)
+        return O.reduce_mean_f32(sl) if wl.grad_dtype == "f32" else O.reduce_mean(sl)
+
     while spent < seconds and done < V:
         n = min(chunk, V - done)
-        sl = [zsgen.host_bf16(wl.seed, grad_stream(0), r, wl.t0, wl.grad_sigma, off + done, n,
-                              p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
-              for r in range(wl.n_d)]
+        sls = [slices(j, n) for j in range(m_count)]
         w = zsgen.host_f32(wl.seed, STREAM_MASTER, 0, 0, wl.master_sigma, off + done, n)
         m = (np.zeros(n, np.float32) if wl.m_sigma is None else
              zsgen.host_f32(wl.seed, STREAM_EXP_AVG, 0, 0, wl.m_sigma, off + done, n))
@@ -76,15 +91,24 @@ def cpu_baseline(wl, shard, seconds: float):
              zsgen.host_f32(wl.seed, STREAM_EXP_AVG_SQ, 0, 0, wl.v_sigma, off + done, n,
                             absval=True))
         t0 = time.perf_counter()
-        g = O.reduce_mean(sl)
+        if m_count == 1:
+            g = reduce(sls[0])
+        else:
+            g = np.empty(n, np.float32)
+            for j in range(m_count):
+                O.accumulate(reduce(sls[j]), j, m_count, g)
         acc.add(g)
         coef = O.clip_coef(acc.value(), wl.max_grad_norm) if wl.max_grad_norm > 0 else None
         O.adamw_f32(h, g, w, m, v, coef=coef)
         O.pack(n, w)
         spent += time.perf_counter() - t0
         done += n
+    what = (f"token-weighted sum of {wl.n_d} {wl.grad_dtype} slices" if weights is not None
+            else f"rank-order mean of {wl.n_d} {wl.grad_dtype} slices")
+    if m_count > 1:
+        what += f", accumulated over {m_count} micro-batches"
     return {"value": done / spent / 1e9, "unit": "G params/s", "cores": 1, "kind": "oracle",
-            "sample": (f"oracle O1-O5 (rank-order mean of {wl.n_d} bf16 slices, fp64 "
+            "sample": (f"oracle O1-O5 ({what}, fp64 "
                        f"exact squared norm, clip, fp32 AdamW, bf16 pack) on the first {done:,} "
                        f"of the {V:,} shard parameters of workload {wl.name}, single "
                        f"thread, {spent:.1f} s of oracle time; input generation untimed"),
@@ -167,7 +191,7 @@ def main():
     wall0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record(stream)
-        if run.clip:
+        if run.has_reduce_pass:
             run.reduce_pass(stream=stream.cuda_stream)
         ev[k][1].record(stream)
         run.update_pass(t, stream=stream.cuda_stream)
@@ -184,16 +208,20 @@ def main():
     red_b, upd_b = run.algorithmic_bytes()
     step_gbps = (red_b + upd_b) / (ms_per_step / 1e3) / 1e9
 
-    # dominant kernel: the fused step (k_step), one launch per unit per step
-    if upd_ms >= red_ms or not run.clip:
-        kname = ("k_step (fp32 mean in, clip, AdamW, bf16 pack)" if run.clip and run.store_mean
+    # dominant kernel: the fused step (k_step, one launch per unit per step)
+    # or the reduction (k_reduce_sqnorm, one launch per unit and micro-batch)
+    if upd_ms >= red_ms or not run.has_reduce_pass:
+        kname = ("k_step (fp32 gradient in, AdamW, bf16 pack)" if run.store_mean
                  else "k_step (bf16 slices in, AdamW, bf16 pack)")
-        launch_ms = upd_ms / run.units
-        launch_bytes = upd_b / run.units
+        launches = run.units
+        launch_ms = upd_ms / launches
+        launch_bytes = upd_b / launches
     else:
-        kname = "k_reduce_sqnorm + k_sqnorm_final (rank-order mean, fp64 squared norm)"
-        launch_ms = red_ms / run.units
-        launch_bytes = red_b / run.units
+        kname = ("k_reduce_sqnorm + k_sqnorm_groups + k_sqnorm_final (rank-order reduction, "
+                 "fp64 squared norm)")
+        launches = run.units * run.micro
+        launch_ms = red_ms / launches
+        launch_bytes = red_b / launches
     achieved = launch_bytes / (launch_ms / 1e3) / 1e9
     traffic = load_traffic(wl.name)
 
@@ -212,16 +240,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "psi": wl.psi, "n_d": wl.n_d, "rank": run.rank,
                    "stage": wl.stage, "units": run.units, "shard_params": params,
-                   "max_grad_norm": wl.max_grad_norm,
+                   "max_grad_norm": wl.max_grad_norm, "grad_dtype": wl.grad_dtype,
+                   "rank_tokens": list(wl.rank_tokens) or None,
+                   "micro_batches": wl.micro_batches,
                    "schedule": ("stored-mean" if run.store_mean else "reread")
-                   if run.clip else "fused"},
+                   if run.has_reduce_pass else "fused"},
         "hbm_gbps": step_gbps,
         "hbm_frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "algorithmic_bytes_per_step": red_b + upd_b,
         "kernel_ms": {"clip_pass": red_ms, "update_pass": upd_ms, "event_span_per_step": span_ms},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kname,
-                     "algorithmic_bytes_per_launch": launch_bytes, "launch_ms": launch_ms},
+                     "algorithmic_bytes_per_launch": launch_bytes, "launch_ms": launch_ms,
+                     "launches_per_step": launches},
         "kernel_src_sha": kernel_source_sha(),
     }
     if not args.no_copy_ceiling:

@@ -26,6 +26,10 @@ ZS_ENULL = -8
 ZS_EUNSUPPORTED = -9
 ZS_EWORKSPACE = -10
 ZS_ELAUNCH = -11
+ZS_EINVAL_REDUCE = -12
+ZS_EZERO_TOKENS = -13
+ZS_GRAD_BF16 = 0
+ZS_GRAD_F32 = 1
 ZS_MAX_RANKS = 64
 ZS_OUT_GATHER = 0
 ZS_OUT_SHARD = 1
@@ -53,6 +57,11 @@ class zs_adamw(C.Structure):
                 ("max_grad_norm", C.c_double)]
 
 
+class zs_reduce(C.Structure):
+    _fields_ = [("grad_dtype", C.c_int32), ("micro", C.c_int32), ("micro_count", C.c_int32),
+                ("reserved", C.c_int32), ("rank_tokens", C.POINTER(C.c_int64))]
+
+
 _lib = None
 
 
@@ -75,6 +84,9 @@ def lib():
         L.zs_comm_bytes.restype = f64
         L.shard_grad_sqnorm.argtypes = [P(zs_shard), vp, vp, vp, C.c_size_t, vp, i32, vp]
         L.shard_grad_sqnorm.restype = C.c_int
+        L.shard_grad_reduce.argtypes = [P(zs_shard), P(zs_reduce), vp, vp, vp, C.c_size_t,
+                                        vp, i32, vp]
+        L.shard_grad_reduce.restype = C.c_int
         L.zero_shard_step.argtypes = [P(zs_shard), P(zs_adamw), vp, vp, vp, f64, vp, vp, vp,
                                       vp, vp]
         L.zero_shard_step.restype = C.c_int
@@ -157,6 +169,30 @@ def shard_grad_sqnorm(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
                                    _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
                                    1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm")
+
+
+def make_reduce(grad_dtype: int = ZS_GRAD_BF16, micro: int = 0, micro_count: int = 1,
+                rank_tokens=None):
+    """A zs_reduce; the token array it points to is kept alive on it."""
+    r = zs_reduce(grad_dtype, micro, micro_count, 0, None)
+    if rank_tokens is not None:
+        arr = (C.c_int64 * len(rank_tokens))(*[int(t) for t in rank_tokens])
+        r.rank_tokens = C.cast(arr, C.POINTER(C.c_int64))
+        r._tokens = arr
+    return r
+
+
+def shard_grad_reduce(s: zs_shard, r: zs_reduce, grad_slices, grad_out, workspace=None,
+                      sqnorm_out=None, accumulate: bool = False, stream=None,
+                      workspace_bytes=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if hasattr(workspace, "numel") else
+                           (zs_workspace_bytes(s) if workspace is not None else 0))
+    _check(lib().shard_grad_reduce(C.byref(s), C.byref(r), _slices(grad_slices),
+                                   _ptr(grad_out), _ptr(workspace), workspace_bytes,
+                                   _ptr(sqnorm_out), 1 if accumulate else 0, _stream(stream)),
+           "shard_grad_reduce")
 
 
 def zero_shard_step(s: zs_shard, h: zs_adamw, grad_slices=None, mean_in=None, sqnorm=None,

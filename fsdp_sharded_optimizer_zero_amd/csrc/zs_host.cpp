@@ -161,6 +161,8 @@ const char* zs_strerror(int code)
     case ZS_EUNSUPPORTED: return "n_d exceeds ZS_MAX_RANKS";
     case ZS_EWORKSPACE: return "workspace smaller than zs_workspace_bytes";
     case ZS_ELAUNCH: return "kernel launch failed";
+    case ZS_EINVAL_REDUCE: return "invalid zs_reduce (dtype, micro-batch index/count or token count)";
+    case ZS_EZERO_TOKENS: return "global token count is zero: the update is rejected";
     default: return "unknown error";
     }
 }

@@ -142,7 +142,7 @@ __device__ __forceinline__ void buffer_store_f4(__amdgpu_buffer_rsrc_t r, uint32
 }
 
 struct SlicePtrs {
-    const uint16_t* p[ZS_MAX_RANKS];
+    const void* p[ZS_MAX_RANKS];   // bf16 or fp32 rows, by the kernel's element type
 };
 
 struct StepArgs {
@@ -166,14 +166,23 @@ struct StepArgs {
 
 struct SqArgs {
     SlicePtrs slices;
-    float* mean_out;
-    double* partials;       // one per block of this launch
+    float wt[ZS_MAX_RANKS]; // token weights (weighted reduction only)
+    float* mean_out;        // the reduced gradient; also read in place when
+                            // it is a micro-batch accumulator
+    double* partials;       // one per block of this launch; null: no norm
     int64_t valid_len;
     int64_t v0;             // first vector of this launch
     int32_t n_d;
     float nd;
     float inv_nd;
+    float micro_count;      // m, the divisor of the last micro-batch
+    float inv_micro_count;  // 1/m when m is a power of two (exact), else 0
 };
+
+// What the clip pass does with the accumulator: write the reduced slice
+// (no accumulation, or the first micro-batch), add it to the accumulator,
+// or add it and divide by the micro-batch count (the last micro-batch).
+enum AccMode { kAccNone = 0, kAccAdd = 1, kAccFinal = 2 };
 
 // ---- bf16 --------------------------------------------------------------------
 
@@ -199,13 +208,50 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 // ---- reduction of the ranks' slices (rank order, fp32) ------------------------
 
-__device__ __forceinline__ void add8(float g[8], u32x4 b)
-{
-    g[0] = g[0] + bf16_lo(b.x); g[1] = g[1] + bf16_hi(b.x);
-    g[2] = g[2] + bf16_lo(b.y); g[3] = g[3] + bf16_hi(b.y);
-    g[4] = g[4] + bf16_lo(b.z); g[5] = g[5] + bf16_hi(b.z);
-    g[6] = g[6] + bf16_lo(b.w); g[7] = g[7] + bf16_hi(b.w);
-}
+// Loading and widening one rank's 8-parameter vector, per element type:
+// bf16 (one 16-byte load, widened exactly) or fp32 (two 16-byte loads).
+template <typename GT>
+struct SliceIO;
+
+template <>
+struct SliceIO<uint16_t> {
+    using Raw = u32x4;
+    template <bool NT>
+    __device__ static Raw fetch(const void* p, int64_t vi)
+    {
+        return load<NT>(reinterpret_cast<const u32x4*>(p) + vi);
+    }
+    __device__ static void widen(const Raw& b, float v[8])
+    {
+        v[0] = bf16_lo(b.x); v[1] = bf16_hi(b.x);
+        v[2] = bf16_lo(b.y); v[3] = bf16_hi(b.y);
+        v[4] = bf16_lo(b.z); v[5] = bf16_hi(b.z);
+        v[6] = bf16_lo(b.w); v[7] = bf16_hi(b.w);
+    }
+    __device__ static float one(const void* p, int64_t i)
+    {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+    }
+};
+
+template <>
+struct SliceIO<float> {
+    struct Raw {
+        f32x4 a, b;
+    };
+    template <bool NT>
+    __device__ static Raw fetch(const void* p, int64_t vi)
+    {
+        const f32x4* q = reinterpret_cast<const f32x4*>(p) + 2 * vi;
+        return Raw{load<NT>(q), load<NT>(q + 1)};
+    }
+    __device__ static void widen(const Raw& b, float v[8])
+    {
+        v[0] = b.a.x; v[1] = b.a.y; v[2] = b.a.z; v[3] = b.a.w;
+        v[4] = b.b.x; v[5] = b.b.y; v[6] = b.b.z; v[7] = b.b.w;
+    }
+    __device__ static float one(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+};
 
 template <int NDT>
 __device__ __forceinline__ float mean_of_sum(float s, float nd, float inv_nd)
@@ -216,40 +262,83 @@ __device__ __forceinline__ float mean_of_sum(float s, float nd, float inv_nd)
     else return s / nd;
 }
 
-// Mean of 8 consecutive elements (vector vi) over the ranks, in rank order.
-template <int NDT, bool NTL = false, typename Args>
+// Reduction of 8 consecutive elements (vector vi) over the ranks, in rank
+// order: the mean (sum from rank 0's value, then one division by N_d), or
+// the token-weighted sum (((w_0*G_0) + (w_1*G_1)) + ..., every product and
+// sum rounded).
+template <typename GT, int NDT, bool WEIGHTED = false, bool NTL = false, typename Args>
 __device__ __forceinline__ void reduce_vec(const Args& a, int64_t vi, float g[8])
 {
+    using IO = SliceIO<GT>;
     const int nd = NDT > 0 ? NDT : a.n_d;
-    const u32x4 x = load<NTL>(reinterpret_cast<const u32x4*>(a.slices.p[0]) + vi);
-    g[0] = bf16_lo(x.x); g[1] = bf16_hi(x.x);
-    g[2] = bf16_lo(x.y); g[3] = bf16_hi(x.y);
-    g[4] = bf16_lo(x.z); g[5] = bf16_hi(x.z);
-    g[6] = bf16_lo(x.w); g[7] = bf16_hi(x.w);
+    float v[8];
+    IO::widen(IO::template fetch<NTL>(a.slices.p[0], vi), v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if constexpr (WEIGHTED) g[k] = a.wt[0] * v[k];
+        else g[k] = v[k];
+    }
     // Loads are issued ZS_RED_GROUP ranks at a time (bounded registers), the
     // additions stay in rank order.
     constexpr int G = ZS_RED_GROUP;
     for (int r0 = 1; r0 < nd; r0 += G) {
-        u32x4 b[G];
+        typename IO::Raw b[G];
 #pragma unroll
         for (int j = 0; j < G; ++j)
-            if (r0 + j < nd) b[j] = load<NTL>(reinterpret_cast<const u32x4*>(a.slices.p[r0 + j]) + vi);
+            if (r0 + j < nd) b[j] = IO::template fetch<NTL>(a.slices.p[r0 + j], vi);
 #pragma unroll
-        for (int j = 0; j < G; ++j)
-            if (r0 + j < nd) add8(g, b[j]);
+        for (int j = 0; j < G; ++j) {
+            if (r0 + j < nd) {
+                IO::widen(b[j], v);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    if constexpr (WEIGHTED) {
+                        const float p = a.wt[r0 + j] * v[k];
+                        g[k] = g[k] + p;
+                    } else {
+                        g[k] = g[k] + v[k];
+                    }
+                }
+            }
+        }
     }
+    if constexpr (!WEIGHTED) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) g[j] = mean_of_sum<NDT>(g[j], a.nd, a.inv_nd);
+        for (int j = 0; j < 8; ++j) g[j] = mean_of_sum<NDT>(g[j], a.nd, a.inv_nd);
+    }
 }
 
-template <int NDT, typename Args>
+template <typename GT, int NDT, bool WEIGHTED = false, typename Args>
 __device__ __forceinline__ float reduce_one(const Args& a, int64_t i)
 {
+    using IO = SliceIO<GT>;
     const int nd = NDT > 0 ? NDT : a.n_d;
-    float s = __uint_as_float(static_cast<uint32_t>(a.slices.p[0][i]) << 16);
-    for (int r = 1; r < nd; ++r)
-        s = s + __uint_as_float(static_cast<uint32_t>(a.slices.p[r][i]) << 16);
-    return mean_of_sum<NDT>(s, a.nd, a.inv_nd);
+    float s = IO::one(a.slices.p[0], i);
+    if constexpr (WEIGHTED) s = a.wt[0] * s;
+    for (int r = 1; r < nd; ++r) {
+        const float x = IO::one(a.slices.p[r], i);
+        if constexpr (WEIGHTED) {
+            const float p = a.wt[r] * x;
+            s = s + p;
+        } else {
+            s = s + x;
+        }
+    }
+    if constexpr (WEIGHTED) return s;
+    else return mean_of_sum<NDT>(s, a.nd, a.inv_nd);
+}
+
+// Micro-batch accumulation of one reduced value: acc + r, and after the last
+// micro-batch (acc + r) / m.
+template <int ACC>
+__device__ __forceinline__ float accumulate1(const SqArgs& a, float acc, float r)
+{
+    float x = acc + r;
+    if constexpr (ACC == kAccFinal) {
+        if (a.inv_micro_count != 0.0f) x = x * a.inv_micro_count;
+        else x = x / a.micro_count;
+    }
+    return x;
 }
 
 // ---- AdamW, one element ---------------------------------------------------------
@@ -306,26 +395,47 @@ __device__ __forceinline__ double block_sum(double q)
 
 // ---- kernels ----------------------------------------------------------------------
 
-// Clip pass 1: mean of the slices (optionally stored) and one fp64 partial
-// sum of squares per block.  Block b of a launch owns kSqVecPerBlock
-// consecutive vectors; thread x reduces vectors base + u*BS + x, u = 0..U-1,
-// issuing all their loads first, and adds their squares in u, then element
-// order.  Only the last block of a shard meets the partial vector or runs
-// past valid_len; it takes the guarded path.
-template <int NDT, bool STORE>
+// Clip pass 1: the reduced gradient of the slices (optionally stored, or
+// accumulated over micro-batches) and one fp64 partial sum of its squares
+// per block.  Block b of a launch owns kSqVecPerBlock consecutive vectors;
+// thread x reduces vectors base + u*BS + x, u = 0..U-1, issuing all their
+// loads first, and adds their squares in u, then element order.  Only the
+// last block of a shard meets the partial vector or runs past valid_len; it
+// takes the guarded path.
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
 __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
 {
+    static_assert(STORE || ACC == kAccNone, "an accumulator is always stored");
     constexpr int BS = kSqThreads, U = ZS_SQ_U;
     const int64_t nfull = a.valid_len >> 3;
     const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kSqVecPerBlock;
     double q = 0.0;
     if (base + kSqVecPerBlock <= nfull) {
+        f32x4 acc0[U], acc1[U];
+        if constexpr (ACC != kAccNone) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out) + 2 * (base + u * BS + threadIdx.x);
+                acc0[u] = load<kSqNtLoad>(p);
+                acc1[u] = load<kSqNtLoad>(p + 1);
+            }
+        }
         float g[U][8];
 #pragma unroll
-        for (int u = 0; u < U; ++u) reduce_vec<NDT, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
-        // The block's kSqVecPerBlock * 32 bytes of the mean (unused when
-        // the mean is not stored: then mean_out is null and nothing is
-        // written through it).
+        for (int u = 0; u < U; ++u)
+            reduce_vec<GT, NDT, WEIGHTED, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
+        if constexpr (ACC != kAccNone) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float ac[8] = {acc0[u].x, acc0[u].y, acc0[u].z, acc0[u].w,
+                                     acc1[u].x, acc1[u].y, acc1[u].z, acc1[u].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) g[u][j] = accumulate1<ACC>(a, ac[j], g[u][j]);
+            }
+        }
+        // The block's kSqVecPerBlock * 32 bytes of the output (unused when
+        // it is not stored: then mean_out is null and nothing is written
+        // through it).
         const __amdgpu_buffer_rsrc_t mr =
             buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
 #pragma unroll
@@ -346,9 +456,15 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
             const int64_t vi = base + u * BS + threadIdx.x;
             if (vi < nfull) {
                 float g[8];
-                reduce_vec<NDT, kSqNtLoad>(a, vi, g);
+                reduce_vec<GT, NDT, WEIGHTED, kSqNtLoad>(a, vi, g);
+                f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
+                if constexpr (ACC != kAccNone) {
+                    const f32x4 c0 = o[0], c1 = o[1];
+                    const float ac[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) g[j] = accumulate1<ACC>(a, ac[j], g[j]);
+                }
                 if constexpr (STORE) {
-                    f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
                     store_f4<kSqNtStore>(o, f32x4{g[0], g[1], g[2], g[3]});
                     store_f4<kSqNtStore>(o + 1, f32x4{g[4], g[5], g[6], g[7]});
                 }
@@ -359,7 +475,8 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
                 }
             } else if (vi == nfull) {
                 for (int64_t i = vi * 8; i < a.valid_len; ++i) {
-                    const float g = reduce_one<NDT>(a, i);
+                    float g = reduce_one<GT, NDT, WEIGHTED>(a, i);
+                    if constexpr (ACC != kAccNone) g = accumulate1<ACC>(a, a.mean_out[i], g);
                     if constexpr (STORE) a.mean_out[i] = g;
                     const double d = g;
                     q = sq_add(q, d);
@@ -367,8 +484,10 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
             }
         }
     }
-    const double t = block_sum<BS>(q);
-    if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
+    if (a.partials) {   // uniform: every thread of the block takes the same branch
+        const double t = block_sum<BS>(q);
+        if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
+    }
 }
 
 // Clip pass 2: group g of block partials, [g*kSqGroup, (g+1)*kSqGroup), is
@@ -402,7 +521,7 @@ __device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c,
                                          int64_t i)
 {
     float g;
-    if constexpr (FROM_SLICES) g = reduce_one<NDT>(a, i);
+    if constexpr (FROM_SLICES) g = reduce_one<uint16_t, NDT>(a, i);
     else g = a.mean[i];
     if constexpr (CLIP) g = g * coef;
     float w = a.w[i], m = a.m[i], v = a.v[i];
@@ -449,7 +568,7 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
     for (int u = 0; u < U; ++u) {
         const int64_t x = vi + u * BS;
         if constexpr (FROM_SLICES) {
-            reduce_vec<NDT>(a, x, g[u]);
+            reduce_vec<uint16_t, NDT>(a, x, g[u]);
         } else {
             const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * x;
             const f32x4 x0 = g4[0], x1 = g4[1];
@@ -606,22 +725,24 @@ int lds_reservation(int per_cu, size_t* bytes)
     return ZS_OK;
 }
 
-template <int NDT, bool STORE>
-int launch_sqnorm_k(const SqArgs& a, int64_t blocks, hipStream_t st)
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
+int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
     const int per_cu = a.n_d >= ZS_SQ_WIDE_ND ? 1 : ZS_SQ_PER_CU;
-    const int rc = lds_reservation<k_reduce_sqnorm<NDT, STORE>>(per_cu, &lds);
+    const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>>(per_cu, &lds);
     if (rc != ZS_OK) return rc;
-    hipLaunchKernelGGL((k_reduce_sqnorm<NDT, STORE>), dim3(blocks), dim3(kSqThreads), lds, st, a);
+    hipLaunchKernelGGL((k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>), dim3(blocks),
+                       dim3(kSqThreads), lds, st, a);
     return launched();
 }
 
+// The bf16 mean, specialized for the common N_d.
 template <int NDT>
 int launch_sqnorm_nd(const SqArgs& a, bool store, int64_t blocks, hipStream_t st)
 {
-    return store ? launch_sqnorm_k<NDT, true>(a, blocks, st)
-                 : launch_sqnorm_k<NDT, false>(a, blocks, st);
+    return store ? launch_reduce_k<uint16_t, NDT, true, false, kAccNone>(a, blocks, st)
+                 : launch_reduce_k<uint16_t, NDT, false, false, kAccNone>(a, blocks, st);
 }
 
 int launch_sqnorm(const SqArgs& a, bool store, int64_t blocks, hipStream_t st)
@@ -636,6 +757,54 @@ int launch_sqnorm(const SqArgs& a, bool store, int64_t blocks, hipStream_t st)
     case 64: return launch_sqnorm_nd<64>(a, store, blocks, st);
     default: return launch_sqnorm_nd<0>(a, store, blocks, st);
     }
+}
+
+// Every other reduction (fp32 slices, token weights, accumulation): N_d = 8
+// specialized, any other N_d through the generic loop.
+template <typename GT, bool WEIGHTED, int ACC>
+int launch_reduce_nd(const SqArgs& a, int64_t blocks, hipStream_t st)
+{
+    if (a.n_d == 8) return launch_reduce_k<GT, 8, true, WEIGHTED, ACC>(a, blocks, st);
+    return launch_reduce_k<GT, 0, true, WEIGHTED, ACC>(a, blocks, st);
+}
+
+template <typename GT, bool WEIGHTED>
+int launch_reduce_acc(const SqArgs& a, int acc, int64_t blocks, hipStream_t st)
+{
+    switch (acc) {
+    case kAccAdd: return launch_reduce_nd<GT, WEIGHTED, kAccAdd>(a, blocks, st);
+    case kAccFinal: return launch_reduce_nd<GT, WEIGHTED, kAccFinal>(a, blocks, st);
+    default: return launch_reduce_nd<GT, WEIGHTED, kAccNone>(a, blocks, st);
+    }
+}
+
+int launch_reduce(const SqArgs& a, bool f32, bool weighted, int acc, int64_t blocks,
+                  hipStream_t st)
+{
+    if (!f32 && !weighted && acc == kAccNone) return launch_sqnorm(a, true, blocks, st);
+    if (f32)
+        return weighted ? launch_reduce_acc<float, true>(a, acc, blocks, st)
+                        : launch_reduce_acc<float, false>(a, acc, blocks, st);
+    return weighted ? launch_reduce_acc<uint16_t, true>(a, acc, blocks, st)
+                    : launch_reduce_acc<uint16_t, false>(a, acc, blocks, st);
+}
+
+// The fixed-order sum of the clip pass's block partials into *sqnorm_out.
+int launch_sqnorm_sums(double* partials, int64_t blocks, double* sqnorm_out, int accumulate,
+                       hipStream_t st)
+{
+    const int64_t groups = sq_groups(blocks);
+    double* group_sums = partials + blocks;
+    if (groups > 0) {
+        hipLaunchKernelGGL(k_sqnorm_groups, dim3(groups), dim3(kFinalThreads), 0, st,
+                           static_cast<const double*>(partials), blocks, group_sums);
+        const int rc = launched();
+        if (rc != ZS_OK) return rc;
+    }
+    hipLaunchKernelGGL(k_sqnorm_final, dim3(1), dim3(kFinalThreads), 0, st,
+                       static_cast<const double*>(group_sums), groups, sqnorm_out,
+                       accumulate ? 1 : 0);
+    return launched();
 }
 
 template <bool FROM_SLICES, int NDT, bool CLIP>
@@ -671,12 +840,12 @@ int launch_step(const StepArgs& a, bool from_slices, bool clip, int64_t blocks, 
     }
 }
 
-int fill_slices(const zs_shard* s, const uint16_t* const* grad_slices, SlicePtrs* out)
+int fill_slices(const zs_shard* s, const void* const* grad_slices, SlicePtrs* out)
 {
     for (int r = 0; r < ZS_MAX_RANKS; ++r) out->p[r] = nullptr;
     if (!grad_slices) return ZS_ENULL;
     for (int r = 0; r < s->n_d; ++r) {
-        const uint16_t* p = grad_slices[r];
+        const void* p = grad_slices[r];
         if (s->valid_len > 0) {
             if (!p) return ZS_ENULL;
             if (!aligned16(p)) return ZS_EALIGN;
@@ -708,7 +877,7 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     if (mean_out && !aligned16(mean_out)) return ZS_EALIGN;
     if (workspace_bytes < zs_workspace_bytes(s)) return ZS_EWORKSPACE;
     SqArgs a;
-    rc = fill_slices(s, grad_slices, &a.slices);
+    rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &a.slices);
     if (rc != ZS_OK) return rc;
     a.mean_out = mean_out;
     a.partials = static_cast<double*>(workspace);
@@ -716,6 +885,8 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     a.n_d = s->n_d;
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
+    a.micro_count = 1.0f;
+    a.inv_micro_count = 1.0f;
     const int64_t blocks = sq_blocks(s->valid_len);
     (void)hipGetLastError();   // drop an error left by an unrelated earlier call
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -726,17 +897,67 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
         a.partials = partials + b0;
         if ((rc = launch_sqnorm(a, mean_out != nullptr, nb, st)) != ZS_OK) return rc;
     }
-    const int64_t groups = sq_groups(blocks);
-    double* group_sums = partials + blocks;
-    if (groups > 0) {
-        hipLaunchKernelGGL(k_sqnorm_groups, dim3(groups), dim3(kFinalThreads), 0, st,
-                           static_cast<const double*>(partials), blocks, group_sums);
-        if ((rc = launched()) != ZS_OK) return rc;
+    return launch_sqnorm_sums(partials, blocks, sqnorm_out, accumulate, st);
+}
+
+extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
+                                 const void* const* grad_slices, float* grad_out,
+                                 void* workspace, size_t workspace_bytes, double* sqnorm_out,
+                                 int32_t accumulate, void* stream)
+{
+    int rc = check_shard(s);
+    if (rc != ZS_OK) return rc;
+    if (!r) return ZS_ENULL;
+    if ((r->grad_dtype != ZS_GRAD_BF16 && r->grad_dtype != ZS_GRAD_F32) || r->reserved != 0 ||
+        r->micro_count < 1 || r->micro < 0 || r->micro >= r->micro_count)
+        return ZS_EINVAL_REDUCE;
+    if (s->valid_len > 0 && !grad_out) return ZS_ENULL;
+    if (grad_out && !aligned16(grad_out)) return ZS_EALIGN;
+    if (sqnorm_out) {
+        if (!workspace) return ZS_ENULL;
+        if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(sqnorm_out) & 7u) != 0)
+            return ZS_EALIGN;
+        if (workspace_bytes < zs_workspace_bytes(s)) return ZS_EWORKSPACE;
     }
-    hipLaunchKernelGGL(k_sqnorm_final, dim3(1), dim3(kFinalThreads), 0, st,
-                       static_cast<const double*>(group_sums), groups, sqnorm_out,
-                       accumulate ? 1 : 0);
-    return launched();
+    SqArgs a;
+    rc = fill_slices(s, grad_slices, &a.slices);
+    if (rc != ZS_OK) return rc;
+    const bool weighted = r->rank_tokens != nullptr;
+    for (int k = 0; k < ZS_MAX_RANKS; ++k) a.wt[k] = 0.0f;
+    if (weighted) {
+        // w_r = n_r / T in double, rounded once; T = 0 rejects the update.
+        double T = 0.0;
+        for (int k = 0; k < s->n_d; ++k) {
+            if (r->rank_tokens[k] < 0) return ZS_EINVAL_REDUCE;
+            T += static_cast<double>(r->rank_tokens[k]);
+        }
+        if (T == 0.0) return ZS_EZERO_TOKENS;
+        for (int k = 0; k < s->n_d; ++k)
+            a.wt[k] = static_cast<float>(static_cast<double>(r->rank_tokens[k]) / T);
+    }
+    const int acc = r->micro == 0 ? kAccNone
+                  : (r->micro == r->micro_count - 1 ? kAccFinal : kAccAdd);
+    a.mean_out = grad_out;
+    a.valid_len = s->valid_len;
+    a.n_d = s->n_d;
+    a.nd = static_cast<float>(s->n_d);
+    a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
+    a.micro_count = static_cast<float>(r->micro_count);
+    a.inv_micro_count = is_pow2(r->micro_count) ? 1.0f / static_cast<float>(r->micro_count)
+                                                : 0.0f;
+    const int64_t blocks = sq_blocks(s->valid_len);
+    (void)hipGetLastError();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    double* partials = sqnorm_out ? static_cast<double*>(workspace) : nullptr;
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        a.v0 = b0 * kSqVecPerBlock;
+        a.partials = partials ? partials + b0 : nullptr;
+        rc = launch_reduce(a, r->grad_dtype == ZS_GRAD_F32, weighted, acc, nb, st);
+        if (rc != ZS_OK) return rc;
+    }
+    if (!sqnorm_out) return ZS_OK;
+    return launch_sqnorm_sums(partials, blocks, sqnorm_out, accumulate, st);
 }
 
 extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,
@@ -764,7 +985,7 @@ extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,
     }
     StepArgs a;
     if (grad_slices) {
-        rc = fill_slices(s, grad_slices, &a.slices);
+        rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &a.slices);
         if (rc != ZS_OK) return rc;
     } else {
         for (int r = 0; r < ZS_MAX_RANKS; ++r) a.slices.p[r] = nullptr;

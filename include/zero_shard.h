@@ -70,6 +70,11 @@ extern "C" {
 #define ZS_EUNSUPPORTED   (-9)   /* n_d > ZS_MAX_RANKS */
 #define ZS_EWORKSPACE    (-10)   /* workspace smaller than zs_workspace_bytes */
 #define ZS_ELAUNCH       (-11)   /* the HIP runtime rejected a kernel launch */
+#define ZS_EINVAL_REDUCE (-12)   /* zs_reduce: unknown grad_dtype, reserved != 0,
+                                    micro outside [0, micro_count), micro_count
+                                    < 1, or a negative token count */
+#define ZS_EZERO_TOKENS  (-13)   /* every rank_tokens entry is 0: the update is
+                                    rejected on every rank; nothing is written */
 
 #define ZS_MAX_RANKS 64          /* gradient slices one call can reduce */
 
@@ -150,6 +155,55 @@ double zs_comm_bytes(double psi, int32_t n_d, int32_t stage, double bytes_per_el
 int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices, float* mean_out,
                       void* workspace, size_t workspace_bytes, double* sqnorm_out,
                       int32_t accumulate, void* stream);
+
+/* Element type of the gradient slices a reduction reads. */
+#define ZS_GRAD_BF16 0   /* bf16, widened exactly to fp32 */
+#define ZS_GRAD_F32  1   /* fp32 (the reduce_dtype=float32 policy) */
+
+/* How shard_grad_reduce combines the ranks' slices and the micro-batches. */
+typedef struct zs_reduce {
+    int32_t grad_dtype;          /* ZS_GRAD_BF16 or ZS_GRAD_F32, every slice */
+    int32_t micro;               /* j, this micro-batch: 0 <= j < micro_count */
+    int32_t micro_count;         /* m >= 1 micro-batches per optimizer step
+                                    (1: no gradient accumulation) */
+    int32_t reserved;            /* must be 0 */
+    const int64_t* rank_tokens;  /* NULL: the mean over ranks; else a host
+                                    array of n_d valid-token counts, and the
+                                    ranks are weighted by n_r / T */
+} zs_reduce;
+
+/* The general clip pass: reduces the ranks' slices of one micro-batch and
+ * accumulates micro-batches into the shard's fp32 gradient.
+ *   "Data parallelism, ZeRO and FSDP", section 3 "Gradient accumulation"
+ *   (ZeRO-2 reduce-scatters after every micro-batch) and section 6 (Llama 3
+ *   reduce-scattered gradients in fp32); "Distributed Training Basics --
+ *   DDP and FSDP", "DDP: replicated state, partitioned examples" (weight
+ *   ranks by valid tokens; a zero global count rejects the update) and
+ *   "Accumulation, clipping and scaling measurements" (clip and step at the
+ *   effective-update boundary).
+ * Per element i < valid_len, in fp32:
+ *   r_i = the mean over ranks, as shard_grad_sqnorm computes it, of bf16 or
+ *         fp32 slices; or, with rank_tokens, ((w_0*G_0[i]) + (w_1*G_1[i]))
+ *         + ... in rank order, w_r = f32(n_r / T) computed in double,
+ *         T = sum of n_r, every product and sum rounded;
+ *   micro == 0:                grad_out[i] = r_i
+ *   0 < micro < m - 1:         grad_out[i] = grad_out[i] + r_i
+ *   micro == m - 1 > 0:        grad_out[i] = (grad_out[i] + r_i) / m
+ * so after the last micro-batch grad_out holds the step's gradient, the
+ * mean over micro-batches, ready for zero_shard_step's mean_in.
+ *   grad_slices  host array of n_d device pointers, each to valid_len
+ *                elements of grad_dtype, 16-byte aligned.
+ *   grad_out     device fp32[valid_len], 16-byte aligned; read and written
+ *                in place for micro > 0.
+ *   workspace, sqnorm_out, accumulate: as for shard_grad_sqnorm, applied to
+ *                the values written.  sqnorm_out may be NULL (then no norm
+ *                and no workspace are needed), e.g. before the last
+ *                micro-batch.
+ * Errors: ZS_ENULL, ZS_EINVAL_*, ZS_EINVAL_REDUCE, ZS_EZERO_TOKENS (nothing
+ * enqueued), ZS_EALIGN, ZS_EUNSUPPORTED, ZS_EWORKSPACE, ZS_ELAUNCH. */
+int shard_grad_reduce(const zs_shard* s, const zs_reduce* r, const void* const* grad_slices,
+                      float* grad_out, void* workspace, size_t workspace_bytes,
+                      double* sqnorm_out, int32_t accumulate, void* stream);
 
 /* The fused optimizer step of this shard.  Exactly one gradient source:
  *   grad_slices  host array of n_d device pointers to bf16[valid_len]

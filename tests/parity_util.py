@@ -17,7 +17,7 @@ import numpy as np
 import oracle as O
 import zsgen
 from zsgen.workloads import (STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_MASTER, Workload,
-                             grad_stream)
+                             grad_key, grad_stream)
 
 FLT_MIN = np.float32(1.1754944e-38)
 REL_BAR = 2e-6          # fp32 state: max relative error against the oracle
@@ -55,22 +55,53 @@ def host_state_at(wl: Workload, unit: int, idx):
     return w, m, v
 
 
-def host_slices(wl: Workload, unit: int, t: int, start: int, n: int):
-    return [zsgen.host_bf16(wl.seed, grad_stream(unit), r, t, wl.grad_sigma, start, n,
+def host_slices(wl: Workload, unit: int, t: int, start: int, n: int, j: int = 0):
+    """Every rank's slice of micro-batch j of step t: bf16 bit patterns or fp32."""
+    key = grad_key(t, j, wl.micro_batches)
+    if wl.grad_dtype == "f32":
+        return [zsgen.host_f32(wl.seed, grad_stream(unit), r, key, wl.grad_sigma, start, n)
+                for r in range(wl.n_d)]
+    return [zsgen.host_bf16(wl.seed, grad_stream(unit), r, key, wl.grad_sigma, start, n,
                             p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
             for r in range(wl.n_d)]
 
 
-def host_slices_at(wl: Workload, unit: int, t: int, idx):
-    return [zsgen.host_bf16_at(wl.seed, grad_stream(unit), r, t, wl.grad_sigma, idx,
+def host_slices_at(wl: Workload, unit: int, t: int, idx, j: int = 0):
+    key = grad_key(t, j, wl.micro_batches)
+    if wl.grad_dtype == "f32":
+        return [zsgen.host_f32_at(wl.seed, grad_stream(unit), r, key, wl.grad_sigma, idx)
+                for r in range(wl.n_d)]
+    return [zsgen.host_bf16_at(wl.seed, grad_stream(unit), r, key, wl.grad_sigma, idx,
                                p_out=wl.outlier_p, sigma_out=wl.outlier_sigma)
             for r in range(wl.n_d)]
+
+
+def oracle_reduce(wl: Workload, sl):
+    """The oracle's reduction of one micro-batch's slices for this workload."""
+    if wl.rank_tokens:
+        return O.reduce_weighted(sl, O.token_weights(wl.rank_tokens))
+    return O.reduce_mean_f32(sl) if wl.grad_dtype == "f32" else O.reduce_mean(sl)
+
+
+def oracle_gradient(wl: Workload, slices_of_micro):
+    """The step's gradient: the reduction of every micro-batch, accumulated."""
+    m = wl.micro_batches
+    if m == 1:
+        return oracle_reduce(wl, slices_of_micro(0))
+    acc = None
+    for j in range(m):
+        r = oracle_reduce(wl, slices_of_micro(j))
+        if acc is None:
+            acc = np.empty_like(r)
+        O.accumulate(r, j, m, acc)
+    return acc
 
 
 # ---- oracle runs ----------------------------------------------------------------------
 
 def oracle_full_run(wl: Workload, rank: int, steps: int, t0: int, shard, other_sqnorm=0.0):
-    """Whole-shard oracle over `steps` steps.  Returns (w, m, v, slot_out, qs, coefs)."""
+    """Whole-shard oracle over `steps` steps of a bf16-mean workload.
+    Returns (w, m, v, slot_out, qs, coefs)."""
     S, off, V = shard.shard_len, shard.shard_offset, shard.valid_len
     w, m, v = host_state(wl, 0, off, V)
     qs, coefs = [], []
@@ -99,15 +130,16 @@ def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
     starts = list(range(0, n, chunk))
 
     def gen(a):
-        return host_slices(wl, unit, t, start + a, min(chunk, n - a))
+        return [host_slices(wl, unit, t, start + a, min(chunk, n - a), j)
+                for j in range(wl.micro_batches)]
 
     with ThreadPoolExecutor(max_workers=1) as ex:
         fut = ex.submit(gen, starts[0]) if starts else None
         for ci, a in enumerate(starts):
-            sl = fut.result()
+            sls = fut.result()
             if ci + 1 < len(starts):
                 fut = ex.submit(gen, starts[ci + 1])
-            g = O.reduce_mean(sl)
+            g = oracle_gradient(wl, lambda j: sls[j])
             acc.add(g)
             if keep_idx is not None:
                 lo, hi = np.searchsorted(keep_idx, [a, a + len(g)])
@@ -124,8 +156,7 @@ def oracle_sampled_step(wl: Workload, unit: int, t: int, shard, idx, coef):
     """Oracle O1, O4, O5 at shard positions idx (relative to the shard), given
     the oracle's clip coefficient (None: no clip).  Returns (w, m, v, bf16)."""
     gidx = shard.shard_offset + np.asarray(idx, np.int64)
-    sl = host_slices_at(wl, unit, t, gidx)
-    g = O.reduce_mean(sl)
+    g = oracle_gradient(wl, lambda j: host_slices_at(wl, unit, t, gidx, j))
     w, m, v = host_state_at(wl, unit, gidx)
     O.adamw_f32(hparams(wl, t), g, w, m, v, coef=coef)
     return w, m, v, O.bf16_rne(w), g

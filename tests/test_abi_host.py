@@ -37,15 +37,15 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) >= {"zs_layout", "zs_workspace_bytes", "zs_state_bytes",
-                          "zs_comm_bytes", "shard_grad_sqnorm", "zero_shard_step",
-                          "shard_pack_gather", "zs_strerror"}
+                          "zs_comm_bytes", "shard_grad_sqnorm", "shard_grad_reduce",
+                          "zero_shard_step", "shard_pack_gather", "zs_strerror"}
     L = C.CDLL(Z.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"{n} declared in zero_shard.h but not exported"
 
 
 def test_strerror_covers_codes():
-    for code in range(-11, 1):
+    for code in range(-13, 1):
         assert Z.zs_strerror(code) != "unknown error"
     assert Z.zs_strerror(-999) == "unknown error"
 
@@ -174,6 +174,39 @@ def test_sqnorm_and_pack_error_paths():
     assert L.shard_pack_gather(C.byref(s), None, FAKE, None) == Z.ZS_ENULL
     assert L.shard_pack_gather(C.byref(s), MIS, FAKE, None) == Z.ZS_EALIGN
     assert L.shard_pack_gather(C.byref(s), FAKE, MIS, None) == Z.ZS_EALIGN
+
+
+def _red(s, r, slices, out=FAKE, ws=None, wsb=None, sq=None):
+    arr = None if slices is None else (C.c_void_p * len(slices))(*slices)
+    if wsb is None:
+        wsb = Z.zs_workspace_bytes(s) if ws is not None else 0
+    return Z.lib().shard_grad_reduce(C.byref(s), None if r is None else C.byref(r), arr, out,
+                                     ws, wsb, sq, 0, None)
+
+
+@no_gpu
+def test_reduce_error_paths():
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    sl = [FAKE] * 4
+    ok = Z.make_reduce()
+    assert _red(s, None, sl) == Z.ZS_ENULL
+    assert _red(s, ok, None) == Z.ZS_ENULL
+    assert _red(s, ok, sl, out=None) == Z.ZS_ENULL
+    assert _red(s, ok, sl, out=MIS) == Z.ZS_EALIGN
+    assert _red(s, ok, [FAKE, MIS, FAKE, FAKE]) == Z.ZS_EALIGN
+    assert _red(s, ok, sl, sq=FAKE) == Z.ZS_ENULL                  # norm needs a workspace
+    assert _red(s, ok, sl, ws=FAKE, wsb=8, sq=FAKE) == Z.ZS_EWORKSPACE
+    assert _red(s, ok, sl, ws=MIS, sq=FAKE) == Z.ZS_EALIGN
+    for bad in (Z.make_reduce(grad_dtype=2), Z.make_reduce(micro=1, micro_count=1),
+                Z.make_reduce(micro=-1, micro_count=2), Z.make_reduce(micro_count=0),
+                Z.make_reduce(rank_tokens=[1, 2, -3, 4])):
+        assert _red(s, bad, sl) == Z.ZS_EINVAL_REDUCE
+    r = Z.make_reduce()
+    r.reserved = 1
+    assert _red(s, r, sl) == Z.ZS_EINVAL_REDUCE
+    # a zero global token count rejects the update before anything is enqueued
+    assert _red(s, Z.make_reduce(rank_tokens=[0, 0, 0, 0]), sl) == Z.ZS_EZERO_TOKENS
+    assert "rejected" in Z.zs_strerror(Z.ZS_EZERO_TOKENS)
 
 
 def test_workspace_is_modest():

@@ -1,0 +1,191 @@
+"""GPU parity of shard_grad_reduce: fp32 gradient slices, token-weighted
+ranks and ZeRO-2 gradient accumulation, through the C ABI, against the CPU
+oracle (or_reduce_mean_f32in, or_reduce_weighted, or_accumulate).
+
+Every expected value comes from the oracle on inputs drawn by the host side of
+the seeded generator or by numpy on the host.  The reductions and the
+accumulator are bit-exact by construction (the same fp32 operations in the
+same order), and that is what is asserted; the squared norm is within 1e-12
+of the oracle's exactly rounded sum.  Run on an MI355X:  pytest -m gpu -s
+"""
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_zero_amd as Z
+import oracle as O
+from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
+from zsgen.workloads import NEXT, WORKLOADS
+from parity_util import (Q_REL_BAR, assert_bf16_close, assert_state_close, coef_is_robust,
+                         log, oracle_sampled_step, oracle_sqnorm_chunked, sample_indices)
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64
+F32_SENTINEL = np.uint32(0x7FC00ABC)     # a NaN pattern the kernels never write
+
+
+@pytest.fixture(autouse=True)
+def _free_gpu_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _rows(slices, n_d, S, V, f32):
+    """Device [n_d, S] rows; beyond V they hold +Inf the kernels must not read."""
+    if f32:
+        rows = torch.full((n_d, S), float("inf"), dtype=torch.float32)
+        for r in range(n_d):
+            rows[r, :V] = torch.from_numpy(slices[r][:V])
+    else:
+        rows = torch.full((n_d, S), 0x7F80, dtype=torch.int16)
+        for r in range(n_d):
+            rows[r, :V] = torch.from_numpy(slices[r][:V].view(np.int16))
+    return rows.cuda()
+
+
+def _oracle_reduce(slices, tokens, f32):
+    if tokens is not None:
+        return O.reduce_weighted(slices, O.token_weights(tokens))
+    return O.reduce_mean_f32(slices) if f32 else O.reduce_mean(slices)
+
+
+def _draw(rng, n_d, V, f32):
+    if f32:
+        return [rng.normal(0, 1e-3, V).astype(np.float32) for _ in range(n_d)]
+    return [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32)) for _ in range(n_d)]
+
+
+def _run_case(psi, n_d, rank, f32, tokens, m, seed):
+    rng = np.random.default_rng(seed)
+    s = Z.zs_layout(psi, n_d, rank, 8, 2)
+    S, V = s.shard_len, s.valid_len
+    esize = 4 if f32 else 2
+    out = torch.from_numpy(np.full(V + GUARD, F32_SENTINEL, np.uint32).view(np.float32)).cuda()
+    ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    acc = np.empty(V, np.float32)
+    for j in range(m):
+        sl = _draw(rng, n_d, V, f32)
+        rows = _rows(sl, n_d, S, V, f32)
+        ptrs = [rows.data_ptr() + esize * S * r for r in range(n_d)]
+        last = j == m - 1
+        r = Z.make_reduce(Z.ZS_GRAD_F32 if f32 else Z.ZS_GRAD_BF16, j, m, tokens)
+        Z.shard_grad_reduce(s, r, ptrs, out, ws if last else None, sq if last else None)
+        torch.cuda.synchronize()
+        O.accumulate(_oracle_reduce(sl, tokens, f32), j, m, acc)
+        got = out.cpu().numpy().view(np.uint32)
+        case = f"psi={psi} n_d={n_d} k={rank} f32={f32} tokens={tokens} j={j}/{m}"
+        assert np.array_equal(got[:V], acc.view(np.uint32)), case
+        assert np.all(got[V:] == F32_SENTINEL), f"{case}: wrote past valid_len"
+        del rows
+    q = O.sqnorm(acc)
+    assert abs(float(sq.item()) - q) <= Q_REL_BAR * max(q, 1e-300), (psi, n_d, rank)
+
+
+def test_reduce_ragged_every_mode():
+    n = 0
+    for psi in (1, 9, 1000, 4099, 100_003):
+        for n_d in (1, 3, 8, 64):
+            if n_d == 64 and psi > 4099:
+                continue
+            for rank in sorted({0, n_d - 1}):
+                for f32 in (False, True):
+                    for weighted in (False, True):
+                        tokens = None
+                        if weighted:
+                            tokens = [(7 * r + 3) % 11 for r in range(n_d)]
+                            if sum(tokens) == 0:
+                                tokens[0] = 1
+                        for m in (1, 3):
+                            _run_case(psi, n_d, rank, f32, tokens, m, seed=n)
+                            n += 1
+    log(f"shard_grad_reduce: {n} ragged cases bit-exact")
+
+
+def test_reduce_bf16_mean_is_the_sqnorm_path():
+    """m = 1, bf16, no weights: the same bits as shard_grad_sqnorm."""
+    rng = np.random.default_rng(31)
+    s = Z.zs_layout(1_000_003, 8, 5, 8, 2)
+    S, V = s.shard_len, s.valid_len
+    sl = _draw(rng, 8, V, False)
+    rows = _rows(sl, 8, S, V, False)
+    ptrs = [rows.data_ptr() + 2 * S * r for r in range(8)]
+    a = torch.empty(V, dtype=torch.float32, device="cuda")
+    b = torch.empty(V, dtype=torch.float32, device="cuda")
+    ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
+    qa = torch.zeros(1, dtype=torch.float64, device="cuda")
+    qb = torch.zeros(1, dtype=torch.float64, device="cuda")
+    Z.shard_grad_sqnorm(s, ptrs, a, ws, qa)
+    Z.shard_grad_reduce(s, Z.make_reduce(), ptrs, b, ws, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert float(qa.item()) == float(qb.item())
+
+
+def test_reduce_token_worked_example_on_gpu():
+    """Ranks with 2 and 6 valid tokens, local mean gradients 3 and 1: 1.5."""
+    s = Z.zs_layout(16, 2, 0, 8, 2)
+    V = s.valid_len
+    for f32 in (False, True):
+        sl = ([np.full(V, 3.0, np.float32), np.full(V, 1.0, np.float32)] if f32 else
+              [O.bf16_rne(np.full(V, 3.0, np.float32)), O.bf16_rne(np.full(V, 1.0, np.float32))])
+        rows = _rows(sl, 2, s.shard_len, V, f32)
+        es = 4 if f32 else 2
+        ptrs = [rows.data_ptr(), rows.data_ptr() + es * s.shard_len]
+        out = torch.zeros(V, dtype=torch.float32, device="cuda")
+        Z.shard_grad_reduce(s, Z.make_reduce(Z.ZS_GRAD_F32 if f32 else Z.ZS_GRAD_BF16,
+                                             rank_tokens=[2, 6]), ptrs, out)
+        torch.cuda.synchronize()
+        assert bool((out == 1.5).all())
+
+
+def test_reduce_zero_tokens_rejects_and_writes_nothing():
+    rng = np.random.default_rng(32)
+    s = Z.zs_layout(5000, 4, 2, 8, 2)
+    S, V = s.shard_len, s.valid_len
+    rows = _rows(_draw(rng, 4, V, False), 4, S, V, False)
+    ptrs = [rows.data_ptr() + 2 * S * r for r in range(4)]
+    out = torch.full((V,), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(Z.ZSError) as e:
+        Z.shard_grad_reduce(s, Z.make_reduce(rank_tokens=[0, 0, 0, 0]), ptrs, out)
+    assert e.value.code == Z.ZS_EZERO_TOKENS
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("name", NEXT)
+def test_next_workloads_full_size(name):
+    """One optimizer step of the 7B ZeRO-2 shard with fp32 slices, token
+    weights, or 4 accumulated micro-batches: the oracle's squared norm over
+    the whole shard, and the whole step at ~1M sampled positions."""
+    wl = WORKLOADS[name]
+    log(f"{name}: allocating and filling on the device")
+    run = ShardRun(wl)
+    run.fill_state(out_fill=0x7FC1)
+    run.fill_grads(wl.t0)
+    run.step(wl.t0)
+    torch.cuda.synchronize()
+    gq = float(run.sqnorm.item())
+    V, s = run.V, run.shard
+    log(f"{name}: GPU Q={gq:.6g}; oracle squared norm over {V:,} params")
+    oq = oracle_sqnorm_chunked(wl, 0, wl.t0, s.shard_offset, V)
+    log(f"{name}: oracle Q={oq:.17g} GPU Q={gq:.17g}")
+    assert abs(gq - oq) <= Q_REL_BAR * oq
+    coef = O.clip_coef(oq, wl.max_grad_norm)
+    idx = sample_indices(V, 1 << 20, seed=7)
+    ow, om, ov, oout, og = oracle_sampled_step(wl, 0, wl.t0, s, idx, coef)
+    d = run.units_data[0]
+    ti = torch.from_numpy(idx).cuda()
+    nb = assert_state_close(f"{name} w", d.w[ti].cpu().numpy(), ow)
+    nb += assert_state_close(f"{name} m", d.m[ti].cpu().numpy(), om)
+    nb += assert_state_close(f"{name} v", d.v[ti].cpu().numpy(), ov)
+    nb += assert_bf16_close(f"{name} out",
+                            d.out[ti + s.shard_offset].cpu().numpy().view(np.uint16), oout)
+    gmean = d.mean[ti].cpu().numpy()
+    assert np.array_equal(gmean.view(np.uint32), og.view(np.uint32)), f"{name}: gradient bits"
+    assert bool((d.out[:s.shard_offset] == 0x7FC1).all())
+    assert bool((d.out[s.shard_offset + s.shard_len:] == 0x7FC1).all())
+    if coef_is_robust(oq, wl.max_grad_norm):
+        assert nb == 0

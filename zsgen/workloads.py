@@ -1,4 +1,4 @@
-"""The five synthetic workloads of the sharded optimizer step.
+"""The synthetic workloads of the sharded optimizer step.
 
 Each workload is one GPU's share of a data-parallel sharded AdamW step, at the
 shape the pages discuss (a ZeRO-1/2 shard of a flat parameter vector, FSDP
@@ -61,6 +61,37 @@ class Workload:
     steps: int = 1
     seed: int = 0
     extra_ranks: tuple = field(default_factory=tuple)   # other ranks also tested
+    grad_dtype: str = "bf16"             # "bf16" or "f32" gradient slices
+    rank_tokens: tuple = ()              # () : plain mean; else valid tokens per rank
+    micro_batches: int = 1               # m: micro-batches per optimizer step
+
+
+def grad_key(t: int, j: int, m: int) -> int:
+    """Generator step key of micro-batch j of optimizer step t (t for m = 1)."""
+    return t * m + j
+
+
+def _splitmix64(x: int) -> int:
+    """SplitMix64 output function (Steele, Lea and Flood 2014)."""
+    x = (x + 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF
+    z = x
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & 0xFFFFFFFFFFFFFFFF
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & 0xFFFFFFFFFFFFFFFF
+    return z ^ (z >> 31)
+
+
+def token_counts(seed: int, n_d: int, seqs: int = 4, max_len: int = 4096,
+                 empty_rank: int = -1) -> tuple:
+    """Valid tokens per rank for a token-weighted workload: each rank holds
+    `seqs` sequences whose valid lengths are uniform in [0, max_len] (the
+    rest is padding); `empty_rank` holds only padding (zero tokens)."""
+    out = []
+    for r in range(n_d):
+        n = 0
+        for q in range(seqs):
+            n += _splitmix64((seed << 32) ^ (r << 16) ^ q) % (max_len + 1)
+        out.append(0 if r == empty_rank else n)
+    return tuple(out)
 
 
 WORKLOADS = {
@@ -91,9 +122,27 @@ WORKLOADS = {
                           stage=3, out_mode="shard", m_sigma=1e-4, v_sigma=1e-6,
                           grad_sigma=5e-4, lr=1.5e-4, beta1=0.9, beta2=0.95,
                           weight_decay=0.1, max_grad_norm=1.0, t0=10, steps=1, seed=4),
+    # The 7B ZeRO-2 shard with the three reductions beyond the bf16 mean:
+    # fp32 gradient slices (reduce_dtype=float32); token-weighted ranks, one
+    # of which holds only padding; ZeRO-2 gradient accumulation over 4
+    # micro-batches (each micro-batch's slices reduced, then accumulated).
+    "zero2_7b_f32grad": Workload(name="zero2_7b_f32grad", psi=7_000_000_000, n_d=8, rank=3,
+                                 align=1, stage=2, out_mode="gather", m_sigma=1e-4,
+                                 v_sigma=1e-6, lr=3e-4, weight_decay=0.1, max_grad_norm=1.0,
+                                 t0=1000, steps=1, seed=5, grad_dtype="f32"),
+    "zero2_7b_tokens": Workload(name="zero2_7b_tokens", psi=7_000_000_000, n_d=8, rank=3,
+                                align=1, stage=2, out_mode="gather", m_sigma=1e-4,
+                                v_sigma=1e-6, lr=3e-4, weight_decay=0.1, max_grad_norm=1.0,
+                                t0=1000, steps=1, seed=6,
+                                rank_tokens=token_counts(6, 8, empty_rank=5)),
+    "zero2_7b_accum4": Workload(name="zero2_7b_accum4", psi=7_000_000_000, n_d=8, rank=3,
+                                align=1, stage=2, out_mode="gather", m_sigma=1e-4,
+                                v_sigma=1e-6, lr=3e-4, weight_decay=0.1, max_grad_norm=1.0,
+                                t0=1000, steps=1, seed=7, micro_batches=4),
 }
 
 ORDER = ["tiny", "gpt2_small", "zero2_7b", "fsdp_llama_units", "zero3_70b"]
+NEXT = ["zero2_7b_f32grad", "zero2_7b_tokens", "zero2_7b_accum4"]
 
 
 def llama_block_params(hidden=4096, ffn=14336, heads=32, kv_heads=8) -> int:
