@@ -532,36 +532,58 @@ __device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c,
     a.out[i] = static_cast<uint16_t>(bf16_rne(w));
 }
 
-// AdamW on U vectors held in registers, bias corrections resolved.
-template <int U, bool CLIP, bool BC1_POW2, bool BC2_POW2>
-__device__ __forceinline__ void adamw_vectors(const StepConsts& c, float coef,
-                                              const float (&g)[U][8], float (&W)[U][8],
-                                              float (&M)[U][8], float (&V)[U][8])
-{
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float gj = g[u][j];
-            if constexpr (CLIP) gj = gj * coef;
-            adamw1<BC1_POW2, BC2_POW2>(c, gj, W[u][j], M[u][j], V[u][j]);
-        }
-    }
-}
-
-// U full vectors at vi, vi + BS, ...: all loads, then the clip coefficient
-// and the arithmetic, then all stores.  The scheduling barrier keeps every
-// load ahead of any arithmetic, so a wave waits for memory once and
-// computes the fp64 clip coefficient while its loads are in flight.  A
-// uniform branch then picks the arithmetic for this step's bias
-// corrections.
-template <int U, int BS, bool FROM_SLICES, int NDT, bool CLIP>
-__device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
+// AdamW on U vectors held in registers, bias corrections resolved, each
+// vector stored as soon as it is computed: while vector u is computed, the
+// loads of vectors u+1.. are still in flight (software pipelining across the
+// thread's vectors).
+template <int U, int BS, bool CLIP, bool BC1_POW2, bool BC2_POW2>
+__device__ __forceinline__ void adamw_store_vectors(const StepArgs& a, const StepConsts& c,
+                                                    float coef, int64_t vi,
+                                                    const float (&g)[U][8], const f32x4 (&w0)[U],
+                                                    const f32x4 (&w1)[U], const f32x4 (&m0)[U],
+                                                    const f32x4 (&m1)[U], const f32x4 (&v0)[U],
+                                                    const f32x4 (&v1)[U])
 {
     f32x4* w4 = reinterpret_cast<f32x4*>(a.w);
     f32x4* m4 = reinterpret_cast<f32x4*>(a.m);
     f32x4* v4 = reinterpret_cast<f32x4*>(a.v);
     u32x4* o4 = reinterpret_cast<u32x4*>(a.out);
+    constexpr bool NT = kStepNtStore;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float W[8] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w, w1[u].x, w1[u].y, w1[u].z, w1[u].w};
+        float M[8] = {m0[u].x, m0[u].y, m0[u].z, m0[u].w, m1[u].x, m1[u].y, m1[u].z, m1[u].w};
+        float V[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float gj = g[u][j];
+            if constexpr (CLIP) gj = gj * coef;
+            adamw1<BC1_POW2, BC2_POW2>(c, gj, W[j], M[j], V[j]);
+        }
+        const int64_t x = vi + u * BS;
+        store_f4<NT>(w4 + 2 * x, f32x4{W[0], W[1], W[2], W[3]});
+        store_f4<NT>(w4 + 2 * x + 1, f32x4{W[4], W[5], W[6], W[7]});
+        store_f4<NT>(m4 + 2 * x, f32x4{M[0], M[1], M[2], M[3]});
+        store_f4<NT>(m4 + 2 * x + 1, f32x4{M[4], M[5], M[6], M[7]});
+        store_f4<NT>(v4 + 2 * x, f32x4{V[0], V[1], V[2], V[3]});
+        store_f4<NT>(v4 + 2 * x + 1, f32x4{V[4], V[5], V[6], V[7]});
+        store<NT>(o4 + x, u32x4{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3]),
+                                pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
+    }
+}
+
+// U full vectors at vi, vi + BS, ...: all loads, then the clip coefficient,
+// then vector by vector the arithmetic and the stores.  The scheduling
+// barrier keeps every load ahead of any arithmetic, so a wave waits for
+// memory once and computes the fp64 clip coefficient while its loads are in
+// flight.  A uniform branch picks the arithmetic for this step's bias
+// corrections.
+template <int U, int BS, bool FROM_SLICES, int NDT, bool CLIP>
+__device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
+{
+    const f32x4* w4 = reinterpret_cast<const f32x4*>(a.w);
+    const f32x4* m4 = reinterpret_cast<const f32x4*>(a.m);
+    const f32x4* v4 = reinterpret_cast<const f32x4*>(a.v);
     float g[U][8];
     f32x4 w0[U], w1[U], m0[U], m1[U], v0[U], v1[U];
 #pragma unroll
@@ -584,35 +606,16 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
     if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
     __builtin_amdgcn_sched_barrier(0);
     const StepConsts c = a.c;
-    float W[U][8], M[U][8], V[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        W[u][0] = w0[u].x; W[u][1] = w0[u].y; W[u][2] = w0[u].z; W[u][3] = w0[u].w;
-        W[u][4] = w1[u].x; W[u][5] = w1[u].y; W[u][6] = w1[u].z; W[u][7] = w1[u].w;
-        M[u][0] = m0[u].x; M[u][1] = m0[u].y; M[u][2] = m0[u].z; M[u][3] = m0[u].w;
-        M[u][4] = m1[u].x; M[u][5] = m1[u].y; M[u][6] = m1[u].z; M[u][7] = m1[u].w;
-        V[u][0] = v0[u].x; V[u][1] = v0[u].y; V[u][2] = v0[u].z; V[u][3] = v0[u].w;
-        V[u][4] = v1[u].x; V[u][5] = v1[u].y; V[u][6] = v1[u].z; V[u][7] = v1[u].w;
-    }
     if (c.bc1_pow2) {
-        if (c.bc2_pow2) adamw_vectors<U, CLIP, true, true>(c, coef, g, W, M, V);
-        else adamw_vectors<U, CLIP, true, false>(c, coef, g, W, M, V);
+        if (c.bc2_pow2)
+            adamw_store_vectors<U, BS, CLIP, true, true>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
+        else
+            adamw_store_vectors<U, BS, CLIP, true, false>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
     } else {
-        if (c.bc2_pow2) adamw_vectors<U, CLIP, false, true>(c, coef, g, W, M, V);
-        else adamw_vectors<U, CLIP, false, false>(c, coef, g, W, M, V);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t x = vi + u * BS;
-        constexpr bool NT = kStepNtStore;
-        store_f4<NT>(w4 + 2 * x, f32x4{W[u][0], W[u][1], W[u][2], W[u][3]});
-        store_f4<NT>(w4 + 2 * x + 1, f32x4{W[u][4], W[u][5], W[u][6], W[u][7]});
-        store_f4<NT>(m4 + 2 * x, f32x4{M[u][0], M[u][1], M[u][2], M[u][3]});
-        store_f4<NT>(m4 + 2 * x + 1, f32x4{M[u][4], M[u][5], M[u][6], M[u][7]});
-        store_f4<NT>(v4 + 2 * x, f32x4{V[u][0], V[u][1], V[u][2], V[u][3]});
-        store_f4<NT>(v4 + 2 * x + 1, f32x4{V[u][4], V[u][5], V[u][6], V[u][7]});
-        store<NT>(o4 + x, u32x4{pack_bf16x2(W[u][0], W[u][1]), pack_bf16x2(W[u][2], W[u][3]),
-                                pack_bf16x2(W[u][4], W[u][5]), pack_bf16x2(W[u][6], W[u][7])});
+        if (c.bc2_pow2)
+            adamw_store_vectors<U, BS, CLIP, false, true>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
+        else
+            adamw_store_vectors<U, BS, CLIP, false, false>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
     }
 }
 
