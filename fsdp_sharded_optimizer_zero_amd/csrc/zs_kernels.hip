@@ -78,6 +78,22 @@ namespace {
 #ifndef ZS_SQ_NT_STORE
 #define ZS_SQ_NT_STORE 1
 #endif
+// Block-to-data mapping.  Blocks are dispatched round robin over the 8 XCDs.
+// Plain: block b takes the b-th span, so neighbouring spans run on
+// different XCDs.  XCD-contiguous: the blocks of XCD x (b = x mod 8) take
+// one contiguous eighth of the spans.  Measured on MI355X: the clip pass
+// over 64 slices is ~3% faster XCD-contiguous (23.0 vs 23.7 ms), over 8
+// slices ~3.5% slower; the step is within 1% either way, and stays plain.
+constexpr int kXcds = 8;
+
+// Logical span of dispatched block b of nb (a bijection on [0, nb)).
+__device__ __forceinline__ int64_t block_span(int64_t b, int64_t nb, bool xcd_contiguous)
+{
+    if (!xcd_contiguous) return b;
+    const int64_t q = nb / kXcds, r = nb % kXcds, x = b % kXcds, i = b / kXcds;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
 // Gradient slices whose loads one thread has in flight at once.
 #ifndef ZS_RED_GROUP
 #define ZS_RED_GROUP 8
@@ -177,6 +193,7 @@ struct SqArgs {
     float inv_nd;
     float micro_count;      // m, the divisor of the last micro-batch
     float inv_micro_count;  // 1/m when m is a power of two (exact), else 0
+    int32_t xcd_contiguous; // block-to-data mapping (see block_span)
 };
 
 // What the clip pass does with the accumulator: write the reduced slice
@@ -408,7 +425,8 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
     static_assert(STORE || ACC == kAccNone, "an accumulator is always stored");
     constexpr int BS = kSqThreads, U = ZS_SQ_U;
     const int64_t nfull = a.valid_len >> 3;
-    const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kSqVecPerBlock;
+    const int64_t span = block_span(blockIdx.x, gridDim.x, a.xcd_contiguous != 0);
+    const int64_t base = a.v0 + span * kSqVecPerBlock;
     double q = 0.0;
     if (base + kSqVecPerBlock <= nfull) {
         f32x4 acc0[U], acc1[U];
@@ -486,7 +504,7 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
     }
     if (a.partials) {   // uniform: every thread of the block takes the same branch
         const double t = block_sum<BS>(q);
-        if (threadIdx.x == 0) a.partials[blockIdx.x] = t;
+        if (threadIdx.x == 0) a.partials[span] = t;
     }
 }
 
@@ -888,6 +906,7 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     a.n_d = s->n_d;
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
+    a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
     a.micro_count = 1.0f;
     a.inv_micro_count = 1.0f;
     const int64_t blocks = sq_blocks(s->valid_len);
@@ -945,6 +964,7 @@ extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
     a.n_d = s->n_d;
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
+    a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
     a.micro_count = static_cast<float>(r->micro_count);
     a.inv_micro_count = is_pow2(r->micro_count) ? 1.0f / static_cast<float>(r->micro_count)
                                                 : 0.0f;
