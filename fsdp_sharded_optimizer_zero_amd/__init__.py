@@ -28,6 +28,7 @@ ZS_EWORKSPACE = -10
 ZS_ELAUNCH = -11
 ZS_EINVAL_REDUCE = -12
 ZS_EZERO_TOKENS = -13
+ZS_EINVAL_UNITS = -14
 ZS_GRAD_BF16 = 0
 ZS_GRAD_F32 = 1
 ZS_MAX_RANKS = 64
@@ -84,6 +85,11 @@ def lib():
         L.zs_comm_bytes.restype = f64
         L.shard_grad_sqnorm.argtypes = [P(zs_shard), vp, vp, vp, C.c_size_t, vp, i32, vp]
         L.shard_grad_sqnorm.restype = C.c_int
+        L.zs_workspace_bytes_units.argtypes = [P(zs_shard), i32]
+        L.zs_workspace_bytes_units.restype = C.c_size_t
+        L.shard_grad_sqnorm_units.argtypes = [P(zs_shard), i32, vp, vp, vp, C.c_size_t, vp,
+                                              i32, vp]
+        L.shard_grad_sqnorm_units.restype = C.c_int
         L.shard_grad_reduce.argtypes = [P(zs_shard), P(zs_reduce), vp, vp, vp, C.c_size_t,
                                         vp, i32, vp]
         L.shard_grad_reduce.restype = C.c_int
@@ -169,6 +175,31 @@ def shard_grad_sqnorm(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
                                    _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
                                    1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm")
+
+
+def zs_workspace_bytes_units(s: zs_shard, units: int) -> int:
+    return lib().zs_workspace_bytes_units(C.byref(s), units)
+
+
+def shard_grad_sqnorm_units(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
+                            accumulate: bool = False, stream=None, workspace_bytes=None) -> None:
+    """grad_slices: flat list of units * n_d device pointers (unit-major);
+    mean_out: None or a list of `units` fp32 buffers (entries may be None)."""
+    units = len(grad_slices) // s.n_d
+    if units * s.n_d != len(grad_slices):
+        raise ValueError("grad_slices must hold units * n_d pointers")
+    means = None
+    if mean_out is not None:
+        if len(mean_out) != units:
+            raise ValueError("one mean buffer per unit")
+        means = (C.c_void_p * units)(*[_ptr(m) for m in mean_out])
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if hasattr(workspace, "numel") else zs_workspace_bytes_units(s, units))
+    _check(lib().shard_grad_sqnorm_units(C.byref(s), units, _slices(grad_slices), means,
+                                         _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
+                                         1 if accumulate else 0, _stream(stream)),
+           "shard_grad_sqnorm_units")
 
 
 def make_reduce(grad_dtype: int = ZS_GRAD_BF16, micro: int = 0, micro_count: int = 1,

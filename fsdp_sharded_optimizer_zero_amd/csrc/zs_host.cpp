@@ -124,6 +124,17 @@ size_t zs_workspace_bytes(const zs_shard* s)
     return static_cast<size_t>(zs::round_up(bytes > 0 ? bytes : 1, 256));
 }
 
+size_t zs_workspace_bytes_units(const zs_shard* s, int32_t units)
+{
+    // units x (partials + group sums), rounded up to 256 bytes
+    if (units < 1) units = 1;
+    const int64_t v = (s && s->valid_len > 0) ? s->valid_len : 0;
+    const int64_t n = zs::sq_blocks(v);
+    const int64_t bytes =
+        static_cast<int64_t>(units) * (n + zs::sq_groups(n)) * static_cast<int64_t>(sizeof(double));
+    return static_cast<size_t>(zs::round_up(bytes > 0 ? bytes : 1, 256));
+}
+
 double zs_state_bytes(double psi, int32_t n_d, int32_t stage, double K)
 {
     if (!(psi > 0.0) || n_d < 1) return -1.0;
@@ -163,6 +174,7 @@ const char* zs_strerror(int code)
     case ZS_ELAUNCH: return "kernel launch failed";
     case ZS_EINVAL_REDUCE: return "invalid zs_reduce (dtype, micro-batch index/count or token count)";
     case ZS_EZERO_TOKENS: return "global token count is zero: the update is rejected";
+    case ZS_EINVAL_UNITS: return "units must be at least 1";
     default: return "unknown error";
     }
 }

@@ -508,29 +508,39 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
     }
 }
 
-// Clip pass 2: group g of block partials, [g*kSqGroup, (g+1)*kSqGroup), is
-// summed by block g (thread x takes x, x + 1024, ... in order; then the
-// block tree).
+// Clip pass 2: group g of unit u's block partials (n per unit, unit-major),
+// [g*kSqGroup, (g+1)*kSqGroup), is summed by block u*ng + g (thread x takes
+// x, x + 1024, ... in order; then the block tree).
 __global__ void __launch_bounds__(kFinalThreads)
-    k_sqnorm_groups(const double* partials, int64_t n, double* group_sums)
+    k_sqnorm_groups(const double* partials, int64_t n, int64_t ng, double* group_sums)
 {
-    const int64_t lo = static_cast<int64_t>(blockIdx.x) * kSqGroup;
+    const int64_t u = blockIdx.x / ng, g = blockIdx.x % ng;
+    const double* p = partials + u * n;
+    const int64_t lo = g * kSqGroup;
     const int64_t hi = lo + kSqGroup < n ? lo + kSqGroup : n;
     double q = 0.0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kFinalThreads) q = q + partials[i];
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kFinalThreads) q = q + p[i];
     const double t = block_sum<kFinalThreads>(q);
     if (threadIdx.x == 0) group_sums[blockIdx.x] = t;
 }
 
-// Clip pass 3: the n group sums, in the same fixed order; the result
-// replaces *out or is added to it.
+// Clip pass 3: unit by unit, in unit order, the unit's ng group sums in
+// the same fixed order; unit 0's sum replaces *out or is added to it, each
+// later unit's sum is added.  This is exactly the sequence of one call per
+// unit with accumulate set from the second unit on.
 __global__ void __launch_bounds__(kFinalThreads)
-    k_sqnorm_final(const double* group_sums, int64_t n, double* out, int accumulate)
+    k_sqnorm_final(const double* group_sums, int64_t ng, int32_t units, double* out,
+                   int accumulate)
 {
-    double q = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += kFinalThreads) q = q + group_sums[i];
-    const double t = block_sum<kFinalThreads>(q);
-    if (threadIdx.x == 0) *out = accumulate ? (*out + t) : t;
+    double total = 0.0;
+    for (int32_t u = 0; u < units; ++u) {
+        double q = 0.0;
+        for (int64_t i = threadIdx.x; i < ng; i += kFinalThreads) q = q + group_sums[u * ng + i];
+        const double t = block_sum<kFinalThreads>(q);
+        if (threadIdx.x == 0) total = u == 0 ? (accumulate ? (*out + t) : t) : (total + t);
+        __syncthreads();   // block_sum's LDS is reused by the next unit
+    }
+    if (threadIdx.x == 0) *out = total;
 }
 
 // One element of the step (the partial last vector).
@@ -810,20 +820,23 @@ int launch_reduce(const SqArgs& a, bool f32, bool weighted, int acc, int64_t blo
                     : launch_reduce_acc<uint16_t, false>(a, acc, blocks, st);
 }
 
-// The fixed-order sum of the clip pass's block partials into *sqnorm_out.
-int launch_sqnorm_sums(double* partials, int64_t blocks, double* sqnorm_out, int accumulate,
-                       hipStream_t st)
+// The fixed-order sum of the clip pass's block partials (units x blocks,
+// unit-major, followed by room for units x groups group sums) into
+// *sqnorm_out.
+int launch_sqnorm_sums(double* partials, int64_t blocks, int32_t units, double* sqnorm_out,
+                       int accumulate, hipStream_t st)
 {
     const int64_t groups = sq_groups(blocks);
-    double* group_sums = partials + blocks;
+    double* group_sums = partials + static_cast<int64_t>(units) * blocks;
     if (groups > 0) {
-        hipLaunchKernelGGL(k_sqnorm_groups, dim3(groups), dim3(kFinalThreads), 0, st,
-                           static_cast<const double*>(partials), blocks, group_sums);
+        hipLaunchKernelGGL(k_sqnorm_groups, dim3(static_cast<int64_t>(units) * groups),
+                           dim3(kFinalThreads), 0, st, static_cast<const double*>(partials),
+                           blocks, groups, group_sums);
         const int rc = launched();
         if (rc != ZS_OK) return rc;
     }
     hipLaunchKernelGGL(k_sqnorm_final, dim3(1), dim3(kFinalThreads), 0, st,
-                       static_cast<const double*>(group_sums), groups, sqnorm_out,
+                       static_cast<const double*>(group_sums), groups, units, sqnorm_out,
                        accumulate ? 1 : 0);
     return launched();
 }
@@ -919,7 +932,52 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
         a.partials = partials + b0;
         if ((rc = launch_sqnorm(a, mean_out != nullptr, nb, st)) != ZS_OK) return rc;
     }
-    return launch_sqnorm_sums(partials, blocks, sqnorm_out, accumulate, st);
+    return launch_sqnorm_sums(partials, blocks, 1, sqnorm_out, accumulate, st);
+}
+
+extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,
+                                       const uint16_t* const* grad_slices,
+                                       float* const* mean_out, void* workspace,
+                                       size_t workspace_bytes, double* sqnorm_out,
+                                       int32_t accumulate, void* stream)
+{
+    int rc = check_shard(s);
+    if (rc != ZS_OK) return rc;
+    if (units < 1) return ZS_EINVAL_UNITS;
+    if (!grad_slices || !workspace || !sqnorm_out) return ZS_ENULL;
+    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(sqnorm_out) & 7u) != 0)
+        return ZS_EALIGN;
+    if (workspace_bytes < zs_workspace_bytes_units(s, units)) return ZS_EWORKSPACE;
+    // validate every unit before enqueueing anything
+    for (int32_t u = 0; u < units; ++u) {
+        SlicePtrs tmp;
+        rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices + u * s->n_d), &tmp);
+        if (rc != ZS_OK) return rc;
+        if (mean_out && mean_out[u] && !aligned16(mean_out[u])) return ZS_EALIGN;
+    }
+    SqArgs a;
+    a.valid_len = s->valid_len;
+    a.n_d = s->n_d;
+    a.nd = static_cast<float>(s->n_d);
+    a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
+    a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
+    a.micro_count = 1.0f;
+    a.inv_micro_count = 1.0f;
+    const int64_t blocks = sq_blocks(s->valid_len);
+    (void)hipGetLastError();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    double* partials = static_cast<double*>(workspace);
+    for (int32_t u = 0; u < units; ++u) {
+        fill_slices(s, reinterpret_cast<const void* const*>(grad_slices + u * s->n_d), &a.slices);
+        a.mean_out = mean_out ? mean_out[u] : nullptr;
+        for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
+            const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+            a.v0 = b0 * kSqVecPerBlock;
+            a.partials = partials + static_cast<int64_t>(u) * blocks + b0;
+            if ((rc = launch_sqnorm(a, a.mean_out != nullptr, nb, st)) != ZS_OK) return rc;
+        }
+    }
+    return launch_sqnorm_sums(partials, blocks, units, sqnorm_out, accumulate, st);
 }
 
 extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
@@ -980,7 +1038,7 @@ extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
         if (rc != ZS_OK) return rc;
     }
     if (!sqnorm_out) return ZS_OK;
-    return launch_sqnorm_sums(partials, blocks, sqnorm_out, accumulate, st);
+    return launch_sqnorm_sums(partials, blocks, 1, sqnorm_out, accumulate, st);
 }
 
 extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,

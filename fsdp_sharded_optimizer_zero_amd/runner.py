@@ -10,7 +10,8 @@ generator, written directly into device memory.  ``step()`` issues exactly
 the library calls of one optimizer step on one stream:
 
 * no clip:   zero_shard_step(grad_slices=...)                 per unit
-* clip:      shard_grad_sqnorm(...)                           per unit
+* clip:      shard_grad_sqnorm(...)                 (one unit), or
+             shard_grad_sqnorm_units(...)           (all FSDP units at once)
              (squared norms summed in unit order: the global norm of the
              FSDP model; the other ranks' shards enter as other_sqnorm),
              then zero_shard_step(mean_in=..., sqnorm=...)    per unit
@@ -30,8 +31,8 @@ from zsgen.workloads import (STREAM_EXP_AVG, STREAM_EXP_AVG_SQ, STREAM_MASTER, W
                              grad_key, grad_stream)
 
 from . import (ZS_GRAD_BF16, ZS_GRAD_F32, ZS_OUT_GATHER, ZS_OUT_SHARD, adamw, make_reduce,
-               shard_grad_reduce, shard_grad_sqnorm, zero_shard_step, zs_layout,
-               zs_workspace_bytes)
+               shard_grad_reduce, shard_grad_sqnorm, shard_grad_sqnorm_units, zero_shard_step,
+               zs_layout, zs_workspace_bytes, zs_workspace_bytes_units)
 
 
 def _empty(n, dtype, device):
@@ -85,8 +86,11 @@ class ShardRun:
                 v=_empty(V, torch.float32, device),
                 mean=_empty(V, torch.float32, device) if self.store_mean else None,
                 out=torch.empty(out_len, dtype=torch.int16, device=device)))
-        self.workspace = torch.empty(zs_workspace_bytes(self.shard) // 8, dtype=torch.float64,
-                                     device=device)
+        # FSDP units of one layout: one clip-pass call for all of them
+        self.grouped_units = self.units > 1 and not self.general
+        wsb = (zs_workspace_bytes_units(self.shard, self.units) if self.grouped_units
+               else zs_workspace_bytes(self.shard))
+        self.workspace = torch.empty(wsb // 8, dtype=torch.float64, device=device)
         self.sqnorm = torch.zeros(1, dtype=torch.float64, device=device)
         self.t = wl.t0
         self.reduce_specs = [make_reduce(ZS_GRAD_F32 if self.f32_grads else ZS_GRAD_BF16, j,
@@ -152,6 +156,12 @@ class ShardRun:
         return [base + self.gsize * S * r for r in range(self.wl.n_d)]
 
     def reduce_pass(self, stream=None):
+        if self.grouped_units:
+            ptrs = [p for d in self.units_data for p in self.slice_ptrs(d)]
+            means = [d.mean for d in self.units_data] if self.store_mean else None
+            shard_grad_sqnorm_units(self.shard, ptrs, means, self.workspace, self.sqnorm,
+                                    stream=stream)
+            return
         for u, d in enumerate(self.units_data):
             if not self.general:
                 shard_grad_sqnorm(self.shard, self.slice_ptrs(d), d.mean, self.workspace,

@@ -75,6 +75,7 @@ extern "C" {
                                     < 1, or a negative token count */
 #define ZS_EZERO_TOKENS  (-13)   /* every rank_tokens entry is 0: the update is
                                     rejected on every rank; nothing is written */
+#define ZS_EINVAL_UNITS  (-14)   /* units < 1 */
 
 #define ZS_MAX_RANKS 64          /* gradient slices one call can reduce */
 
@@ -155,6 +156,30 @@ double zs_comm_bytes(double psi, int32_t n_d, int32_t stage, double bytes_per_el
 int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices, float* mean_out,
                       void* workspace, size_t workspace_bytes, double* sqnorm_out,
                       int32_t accumulate, void* stream);
+
+/* Bytes of device workspace shard_grad_sqnorm_units needs for `units`
+ * units of layout s: units x what one shard needs (1.7 MB per 875M
+ * parameters of a unit).  Host only. */
+size_t zs_workspace_bytes_units(const zs_shard* s, int32_t units);
+
+/* The clip pass of `units` FSDP units that share one layout (e.g. identical
+ * transformer blocks), as one call: the same result, bit for bit, as
+ * shard_grad_sqnorm on unit 0 with `accumulate` followed by
+ * shard_grad_sqnorm on units 1.. with accumulate = 1 -- the global squared
+ * norm over the units ("Data parallelism, ZeRO and FSDP", section 7: the
+ * norm of sharded gradients sums the squared shard norms), each unit's sum
+ * taken in the fixed per-shard order and added in unit order -- but with
+ * two partial-sum kernels in all instead of two per unit.
+ *   grad_slices  host array of units x n_d device pointers, unit-major
+ *                (unit u's rank r slice at [u*n_d + r]).
+ *   mean_out     NULL, or a host array of `units` device pointers (each
+ *                fp32[valid_len] or NULL) receiving each unit's mean.
+ *   workspace    >= zs_workspace_bytes_units(s, units) bytes.
+ * Errors: as shard_grad_sqnorm, plus ZS_EINVAL_UNITS; every unit's
+ * pointers are checked before anything is enqueued. */
+int shard_grad_sqnorm_units(const zs_shard* s, int32_t units, const uint16_t* const* grad_slices,
+                            float* const* mean_out, void* workspace, size_t workspace_bytes,
+                            double* sqnorm_out, int32_t accumulate, void* stream);
 
 /* Element type of the gradient slices a reduction reads. */
 #define ZS_GRAD_BF16 0   /* bf16, widened exactly to fp32 */

@@ -38,6 +38,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) >= {"zs_layout", "zs_workspace_bytes", "zs_state_bytes",
                           "zs_comm_bytes", "shard_grad_sqnorm", "shard_grad_reduce",
+                          "shard_grad_sqnorm_units", "zs_workspace_bytes_units",
                           "zero_shard_step", "shard_pack_gather", "zs_strerror"}
     L = C.CDLL(Z.LIB_PATH)
     for n in names:
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_strerror_covers_codes():
-    for code in range(-13, 1):
+    for code in range(-14, 1):
         assert Z.zs_strerror(code) != "unknown error"
     assert Z.zs_strerror(-999) == "unknown error"
 
@@ -207,6 +208,33 @@ def test_reduce_error_paths():
     # a zero global token count rejects the update before anything is enqueued
     assert _red(s, Z.make_reduce(rank_tokens=[0, 0, 0, 0]), sl) == Z.ZS_EZERO_TOKENS
     assert "rejected" in Z.zs_strerror(Z.ZS_EZERO_TOKENS)
+
+
+@no_gpu
+def test_sqnorm_units_error_paths():
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    L = Z.lib()
+    units = 3
+    wsb = Z.zs_workspace_bytes_units(s, units)
+    assert wsb >= units * (Z.zs_workspace_bytes(s) - 256)
+
+    def call(u=units, slices=None, ws=FAKE, wsbytes=wsb, sq=FAKE, means=None):
+        sl = slices if slices is not None else [FAKE] * (s.n_d * max(u, 1))
+        arr = (C.c_void_p * len(sl))(*sl)
+        m = None if means is None else (C.c_void_p * len(means))(*means)
+        return L.shard_grad_sqnorm_units(C.byref(s), u, arr, m, ws, wsbytes, sq, 0, None)
+
+    assert call(u=0) == Z.ZS_EINVAL_UNITS
+    assert call(ws=None) == Z.ZS_ENULL
+    assert call(sq=None) == Z.ZS_ENULL
+    assert call(wsbytes=wsb - 8) == Z.ZS_EWORKSPACE
+    bad = [FAKE] * (s.n_d * units)
+    bad[2 * s.n_d + 1] = MIS                      # a slice of the last unit
+    assert call(slices=bad) == Z.ZS_EALIGN
+    bad[2 * s.n_d + 1] = None
+    assert call(slices=bad) == Z.ZS_ENULL
+    assert call(means=[FAKE, MIS, None]) == Z.ZS_EALIGN
+    assert "units" in Z.zs_strerror(Z.ZS_EINVAL_UNITS)
 
 
 def test_workspace_is_modest():

@@ -189,3 +189,39 @@ def test_next_workloads_full_size(name):
     assert bool((d.out[s.shard_offset + s.shard_len:] == 0x7FC1).all())
     if coef_is_robust(oq, wl.max_grad_norm):
         assert nb == 0
+
+
+@pytest.mark.parametrize("n_d,units", [(3, 1), (8, 3), (8, 5), (64, 2)])
+def test_sqnorm_units_equals_per_unit_calls(n_d, units):
+    """shard_grad_sqnorm_units over several FSDP units gives the bits of one
+    shard_grad_sqnorm per unit (accumulate from the second on): the same
+    means and the same squared norm, with and without a prior value."""
+    rng = np.random.default_rng(40 + units)
+    psi = 300_007 if n_d < 64 else 40_009
+    s = Z.zs_layout(psi, n_d, n_d - 1, 8, 3)
+    S, V = s.shard_len, s.valid_len
+    rows = [_rows(_draw(rng, n_d, V, False), n_d, S, V, False) for _ in range(units)]
+    ptrs = [r.data_ptr() + 2 * S * k for r in rows for k in range(n_d)]
+    means_a = [torch.empty(max(V, 8), dtype=torch.float32, device="cuda") for _ in range(units)]
+    means_b = [torch.empty(max(V, 8), dtype=torch.float32, device="cuda") for _ in range(units)]
+    ws1 = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
+    wsu = torch.empty(Z.zs_workspace_bytes_units(s, units) // 8, dtype=torch.float64,
+                      device="cuda")
+    for prior in (None, 3.25):
+        qa = torch.full((1,), 0.0 if prior is None else prior, dtype=torch.float64, device="cuda")
+        qb = qa.clone()
+        for u in range(units):
+            Z.shard_grad_sqnorm(s, ptrs[u * n_d:(u + 1) * n_d], means_a[u], ws1, qa,
+                                accumulate=(u > 0 or prior is not None))
+        Z.shard_grad_sqnorm_units(s, ptrs, means_b, wsu, qb, accumulate=prior is not None)
+        torch.cuda.synchronize()
+        assert float(qa.item()) == float(qb.item()), (prior, qa.item(), qb.item())
+        for a, b in zip(means_a, means_b):
+            assert torch.equal(a[:V].view(torch.int32), b[:V].view(torch.int32))
+    # and against the oracle's exact norm over all units
+    acc = O.SqAcc()
+    for r in rows:
+        sl = [r[k, :V].cpu().numpy().view(np.uint16).copy() for k in range(n_d)]
+        acc.add(O.reduce_mean(sl))
+    oq = acc.value() + 3.25
+    assert abs(float(qb.item()) - oq) <= Q_REL_BAR * oq
