@@ -34,17 +34,21 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed PMC
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"k_step_{workload}_pmc.json")
+def load_traffic(workload: str, kernel_prefix: str):
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE,
+    scaled by the plain copy's reading) from the committed counter summary of
+    this workload, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         p = json.load(f)
     if p.get("kernel_src_sha") != kernel_source_sha():
         return None
-    return p.get("traffic_bytes_per_launch")
+    hits = [k for k in p.get("kernels", {}) if k.startswith(kernel_prefix)]
+    if not hits:
+        return None
+    return max(p["kernels"][k]["hbm_bytes_per_dispatch"] for k in hits)
 
 
 def cpu_baseline(wl, shard, seconds: float):
@@ -223,7 +227,8 @@ def main():
         launch_ms = red_ms / launches
         launch_bytes = red_b / launches
     achieved = launch_bytes / (launch_ms / 1e3) / 1e9
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name, "k_step" if kname.startswith("k_step") else
+                           "k_reduce_sqnorm")
 
     out = {
         "metric": METRIC,
