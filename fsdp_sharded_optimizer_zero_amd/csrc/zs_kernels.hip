@@ -95,15 +95,16 @@ __device__ __forceinline__ int64_t block_span(int64_t b, int64_t nb, bool xcd_co
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
-// fp32 slices in the clip pass's full blocks: 0 = a lane reads 8
-// consecutive elements (two 16-byte loads 16 bytes apart, so a wave's load
-// covers 2 KB at a 32-byte stride); 1 = a lane reads 4 + 4 elements 256
-// apart, so every 16-byte load of a wave covers one contiguous kilobyte.
-// Measured on MI355X (8 fp32 slices of 875M parameters): 6.07 -> 5.43 ms
-// (with one block per CU).
-#ifndef ZS_F32_CONTIG
-#define ZS_F32_CONTIG 1
-#endif
+// Lane mapping of the clip pass's full blocks.  Plain: a lane reads the 8
+// consecutive elements of one vector (bf16: one 16-byte load per slice; fp32:
+// two 16-byte loads 16 bytes apart, so a wave's access covers 2 KB at a
+// 32-byte stride, as do the fp32 mean and accumulator accesses).
+// Contiguous: a lane takes 4 + 4 elements 256 apart, so every load or store
+// instruction of a wave covers one contiguous span (1 KB for fp32, 512 B for
+// bf16 read as 8-byte halves).  Measured on MI355X: contiguous is faster for
+// fp32 slices (6.07 -> 5.43 ms, 8 slices of 875M) and for 8 bf16 slices
+// (2.93 -> 2.83 ms; accumulation passes 13.3 -> 13.0 ms for 4), slower by
+// ~1% for 64 bf16 slices, which keep the plain mapping.
 
 // Gradient slices whose loads one thread has in flight at once.
 #ifndef ZS_RED_GROUP
@@ -205,6 +206,7 @@ struct SqArgs {
     float micro_count;      // m, the divisor of the last micro-batch
     float inv_micro_count;  // 1/m when m is a power of two (exact), else 0
     int32_t xcd_contiguous; // block-to-data mapping (see block_span)
+    int32_t contiguous;     // lane mapping of full blocks (see k_reduce_sqnorm)
 };
 
 // What the clip pass does with the accumulator: write the reduced slice
@@ -449,10 +451,10 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
     const int64_t span = block_span(blockIdx.x, gridDim.x, a.xcd_contiguous != 0);
     const int64_t base = a.v0 + span * kSqVecPerBlock;
     double q = 0.0;
-    constexpr bool kContig = ZS_F32_CONTIG && std::is_same<GT, float>::value && U == 1 &&
-                             BS % 64 == 0;
-    if (kContig && base + kSqVecPerBlock <= nfull) {
-      if constexpr (kContig) {
+    constexpr bool kF32 = std::is_same<GT, float>::value;
+    constexpr bool kCanContig = U == 1 && BS % 64 == 0;
+    if (kCanContig && a.contiguous && base + kSqVecPerBlock <= nfull) {
+      if constexpr (kCanContig) {
         // f32x4 indices of this lane's two groups of four elements
         const int64_t i0 = 2 * base + (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
         const int64_t i1 = i0 + 64;
@@ -466,9 +468,16 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
         reduce_fetched<GT, NDT, WEIGHTED>(
             a,
             [&](int r) {
-                const f32x4* q4 = static_cast<const f32x4*>(a.slices.p[r]);
-                return typename SliceIO<float>::Raw{load<kSqNtLoad>(q4 + i0),
-                                                    load<kSqNtLoad>(q4 + i1)};
+                if constexpr (kF32) {
+                    const f32x4* q4 = static_cast<const f32x4*>(a.slices.p[r]);
+                    return typename SliceIO<float>::Raw{load<kSqNtLoad>(q4 + i0),
+                                                        load<kSqNtLoad>(q4 + i1)};
+                } else {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2* q2 = static_cast<const u32x2*>(a.slices.p[r]);
+                    const u32x2 lo = load<kSqNtLoad>(q2 + i0), hi = load<kSqNtLoad>(q2 + i1);
+                    return u32x4{lo.x, lo.y, hi.x, hi.y};
+                }
             },
             g);
         if constexpr (ACC != kAccNone) {
@@ -822,9 +831,11 @@ template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
 int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
-    // fp32 slices (16 loads per thread at N_d = 8) and wide bf16 reductions
-    // keep enough bytes in flight at one block per CU
-    const bool wide = std::is_same<GT, float>::value || a.n_d >= ZS_SQ_WIDE_ND;
+    // fp32 slices (16 loads per thread at N_d = 8), accumulation passes
+    // (the accumulator's loads on top) and wide bf16 reductions keep enough
+    // bytes in flight at one block per CU
+    const bool wide = std::is_same<GT, float>::value || ACC != kAccNone ||
+                      a.n_d >= ZS_SQ_WIDE_ND;
     const int per_cu = wide ? 1 : ZS_SQ_PER_CU;
     const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>>(per_cu, &lds);
     if (rc != ZS_OK) return rc;
@@ -985,6 +996,7 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
     a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
+    a.contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 0 : 1;
     a.micro_count = 1.0f;
     a.inv_micro_count = 1.0f;
     const int64_t blocks = sq_blocks(s->valid_len);
@@ -1026,6 +1038,7 @@ extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
     a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
+    a.contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 0 : 1;
     a.micro_count = 1.0f;
     a.inv_micro_count = 1.0f;
     const int64_t blocks = sq_blocks(s->valid_len);
@@ -1088,6 +1101,7 @@ extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
     a.nd = static_cast<float>(s->n_d);
     a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
     a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
+    a.contiguous = (r->grad_dtype == ZS_GRAD_F32 || s->n_d < ZS_SQ_WIDE_ND) ? 1 : 0;
     a.micro_count = static_cast<float>(r->micro_count);
     a.inv_micro_count = is_pow2(r->micro_count) ? 1.0f / static_cast<float>(r->micro_count)
                                                 : 0.0f;
