@@ -2,15 +2,16 @@
 // the C-ABI entry points that validate arguments and launch them.
 //
 // Every kernel is a streaming, HBM-bound, elementwise pass (nothing here is
-// a contraction, so no MFMA): 64-lane waves, each lane owns 8 consecutive
-// parameters so that every operand moves as one 16-byte load or store
-// (8 bf16 = 16 B, 8 fp32 = 2 x 16 B).  Grids are one-shot: one thread per
-// 8-parameter vector and hundreds of thousands of blocks, dispatched in
-// index order, so the addresses in flight form one window that sweeps the
-// arrays front to back (on MI355X this streams at ~6.3-6.9 TB/s, where a
-// persistent grid-stride loop levels off near 5 TB/s).  The last vector of
-// a shard may be partial; it and the bf16 pads are handled element by
-// element by the thread that owns it.
+// a contraction, so no MFMA): 64-lane waves, each lane owns 8 parameters and
+// moves every operand in 16-byte (or, for bf16 in the clip pass's
+// contiguous mapping, 8-byte) vector loads and stores.  Grids are one-shot:
+// one thread per 8-parameter vector and hundreds of thousands of blocks,
+// dispatched in index order, so the addresses in flight form one window
+// that sweeps the arrays front to back (on MI355X a plain copy launched so
+// streams at 6.2 TB/s and a read at 6.9 TB/s, where a persistent
+// grid-stride loop levels off near 5 TB/s).  The last vector of a shard may
+// be partial; it and the bf16 pads are handled element by element by the
+// thread that owns it.
 //
 // What is computed ("Data parallelism, ZeRO and FSDP", Lesson 8):
 //  - the reduce-scatter's local reduction: the rank gradients are averaged
@@ -56,7 +57,8 @@ namespace {
 // Measured on MI355X: the step over an 875M-parameter shard is ~7% faster
 // at two 256-thread blocks per CU than uncapped (one block leaves its
 // division and square-root chain exposed); the clip pass is fastest at two
-// 512-thread blocks per CU over 8 slices and at one over 64.
+// 512-thread blocks per CU over 8 bf16 slices, and at one for 64 slices,
+// for fp32 slices and for the accumulation passes (more loads per thread).
 #ifndef ZS_STEP_PER_CU
 #define ZS_STEP_PER_CU 2
 #endif
@@ -139,9 +141,9 @@ __device__ __forceinline__ void store(T* p, T v)
     else *p = v;
 }
 
-// Non-temporal 16-byte store of four floats, issued as an integer vector:
-// the optimizer rebuilds float-vector stores from their scalar lanes and
-// drops the non-temporal hint on the way.
+// 16-byte store of four floats, non-temporal if NT.  (The step's stores
+// keep the hint; for the clip pass's stores the optimizer drops it, so that
+// pass uses buffer_store_f4 below.)
 template <bool NT>
 __device__ __forceinline__ void store_f4(f32x4* p, f32x4 v)
 {
@@ -292,13 +294,11 @@ __device__ __forceinline__ float mean_of_sum(float s, float nd, float inv_nd)
     else return s / nd;
 }
 
-// Reduction of 8 consecutive elements (vector vi) over the ranks, in rank
-// order: the mean (sum from rank 0's value, then one division by N_d), or
-// the token-weighted sum (((w_0*G_0) + (w_1*G_1)) + ..., every product and
-// sum rounded).
-//
-// `fetch(r)` returns rank r's raw vector; reduce_vec fetches the 8
-// consecutive elements of vector vi.
+// Reduction of one lane's 8 elements over the ranks, in rank order: the
+// mean (sum from rank 0's value, then one division by N_d), or the
+// token-weighted sum (((w_0*G_0) + (w_1*G_1)) + ..., every product and sum
+// rounded).  `fetch(r)` returns rank r's raw 8 elements; reduce_vec fetches
+// the 8 consecutive elements of vector vi.
 template <typename GT, int NDT, bool WEIGHTED, typename Fetch, typename Args>
 __device__ __forceinline__ void reduce_fetched(const Args& a, Fetch fetch, float g[8])
 {
@@ -435,13 +435,113 @@ __device__ __forceinline__ double block_sum(double q)
 
 // ---- kernels ----------------------------------------------------------------------
 
+// A full block in the contiguous lane mapping (one vector's worth of
+// elements per thread); adds the thread's squares to q.
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
+__device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t base, double& q)
+{
+    constexpr bool kF32 = std::is_same<GT, float>::value;
+    // f32x4 indices of this lane's two groups of four elements
+    const int64_t i0 = 2 * base + (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
+    const int64_t i1 = i0 + 64;
+    f32x4 c0{}, c1{};
+    if constexpr (ACC != kAccNone) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out);
+        c0 = load<kSqNtLoad>(p + i0);
+        c1 = load<kSqNtLoad>(p + i1);
+    }
+    float g[8];
+    reduce_fetched<GT, NDT, WEIGHTED>(
+        a,
+        [&](int r) {
+            if constexpr (kF32) {
+                const f32x4* q4 = static_cast<const f32x4*>(a.slices.p[r]);
+                return typename SliceIO<float>::Raw{load<kSqNtLoad>(q4 + i0),
+                                                    load<kSqNtLoad>(q4 + i1)};
+            } else {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2* q2 = static_cast<const u32x2*>(a.slices.p[r]);
+                const u32x2 lo = load<kSqNtLoad>(q2 + i0), hi = load<kSqNtLoad>(q2 + i1);
+                return u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+        },
+        g);
+    if constexpr (ACC != kAccNone) {
+        const float ac[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g[j] = accumulate1<ACC>(a, ac[j], g[j]);
+    }
+    if constexpr (STORE) {
+        const __amdgpu_buffer_rsrc_t mr =
+            buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
+        buffer_store_f4<kSqNtStore>(mr, static_cast<uint32_t>((i0 - 2 * base) * 16),
+                                    f32x4{g[0], g[1], g[2], g[3]});
+        buffer_store_f4<kSqNtStore>(mr, static_cast<uint32_t>((i1 - 2 * base) * 16),
+                                    f32x4{g[4], g[5], g[6], g[7]});
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double d = g[j];
+        q = sq_add(q, d);
+    }
+}
+
+// A full block in the plain lane mapping (U vectors per thread).
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
+__device__ __forceinline__ void reduce_block_plain(const SqArgs& a, int64_t base, double& q)
+{
+    constexpr int BS = kSqThreads, U = ZS_SQ_U;
+    f32x4 acc0[U], acc1[U];
+    if constexpr (ACC != kAccNone) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out) + 2 * (base + u * BS + threadIdx.x);
+            acc0[u] = load<kSqNtLoad>(p);
+            acc1[u] = load<kSqNtLoad>(p + 1);
+        }
+    }
+    float g[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        reduce_vec<GT, NDT, WEIGHTED, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
+    if constexpr (ACC != kAccNone) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float ac[8] = {acc0[u].x, acc0[u].y, acc0[u].z, acc0[u].w,
+                                 acc1[u].x, acc1[u].y, acc1[u].z, acc1[u].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) g[u][j] = accumulate1<ACC>(a, ac[j], g[u][j]);
+        }
+    }
+    // The block's kSqVecPerBlock * 32 bytes of the output (unused when
+    // it is not stored: then mean_out is null and nothing is written
+    // through it).
+    const __amdgpu_buffer_rsrc_t mr =
+        buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (STORE) {
+            const uint32_t off = static_cast<uint32_t>((u * BS + threadIdx.x) * 32);
+            buffer_store_f4<kSqNtStore>(mr, off, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
+            buffer_store_f4<kSqNtStore>(mr, off + 16, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const double d = g[u][j];
+            q = sq_add(q, d);
+        }
+    }
+}
+
 // Clip pass 1: the reduced gradient of the slices (optionally stored, or
 // accumulated over micro-batches) and one fp64 partial sum of its squares
-// per block.  Block b of a launch owns kSqVecPerBlock consecutive vectors;
-// thread x reduces vectors base + u*BS + x, u = 0..U-1, issuing all their
-// loads first, and adds their squares in u, then element order.  Only the
-// last block of a shard meets the partial vector or runs past valid_len; it
-// takes the guarded path.
+// per block.  Block span s (see block_span) owns kSqVecPerBlock consecutive
+// vectors.  Contiguous mapping: lane l of the block's wave w takes elements
+// 4l..4l+3 and 256+4l..256+4l+3 of the wave's 512.  Plain mapping: thread x
+// reduces vectors base + u*BS + x, u = 0..U-1, issuing all their loads
+// first.  Either way a thread adds its squares in a fixed order, and only
+// the last block of a shard, which meets the partial vector or runs past
+// valid_len, takes the guarded element-wise path.
 template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
 __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
 {
@@ -451,94 +551,12 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
     const int64_t span = block_span(blockIdx.x, gridDim.x, a.xcd_contiguous != 0);
     const int64_t base = a.v0 + span * kSqVecPerBlock;
     double q = 0.0;
-    constexpr bool kF32 = std::is_same<GT, float>::value;
-    constexpr bool kCanContig = U == 1 && BS % 64 == 0;
-    if (kCanContig && a.contiguous && base + kSqVecPerBlock <= nfull) {
-      if constexpr (kCanContig) {
-        // f32x4 indices of this lane's two groups of four elements
-        const int64_t i0 = 2 * base + (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
-        const int64_t i1 = i0 + 64;
-        f32x4 c0{}, c1{};
-        if constexpr (ACC != kAccNone) {
-            const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out);
-            c0 = load<kSqNtLoad>(p + i0);
-            c1 = load<kSqNtLoad>(p + i1);
-        }
-        float g[8];
-        reduce_fetched<GT, NDT, WEIGHTED>(
-            a,
-            [&](int r) {
-                if constexpr (kF32) {
-                    const f32x4* q4 = static_cast<const f32x4*>(a.slices.p[r]);
-                    return typename SliceIO<float>::Raw{load<kSqNtLoad>(q4 + i0),
-                                                        load<kSqNtLoad>(q4 + i1)};
-                } else {
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    const u32x2* q2 = static_cast<const u32x2*>(a.slices.p[r]);
-                    const u32x2 lo = load<kSqNtLoad>(q2 + i0), hi = load<kSqNtLoad>(q2 + i1);
-                    return u32x4{lo.x, lo.y, hi.x, hi.y};
-                }
-            },
-            g);
-        if constexpr (ACC != kAccNone) {
-            const float ac[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) g[j] = accumulate1<ACC>(a, ac[j], g[j]);
-        }
-        if constexpr (STORE) {
-            const __amdgpu_buffer_rsrc_t mr =
-                buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
-            buffer_store_f4<kSqNtStore>(mr, static_cast<uint32_t>((i0 - 2 * base) * 16),
-                                        f32x4{g[0], g[1], g[2], g[3]});
-            buffer_store_f4<kSqNtStore>(mr, static_cast<uint32_t>((i1 - 2 * base) * 16),
-                                        f32x4{g[4], g[5], g[6], g[7]});
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const double d = g[j];
-            q = sq_add(q, d);
-        }
-      }
-    } else if (base + kSqVecPerBlock <= nfull) {
-        f32x4 acc0[U], acc1[U];
-        if constexpr (ACC != kAccNone) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out) + 2 * (base + u * BS + threadIdx.x);
-                acc0[u] = load<kSqNtLoad>(p);
-                acc1[u] = load<kSqNtLoad>(p + 1);
-            }
-        }
-        float g[U][8];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            reduce_vec<GT, NDT, WEIGHTED, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
-        if constexpr (ACC != kAccNone) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float ac[8] = {acc0[u].x, acc0[u].y, acc0[u].z, acc0[u].w,
-                                     acc1[u].x, acc1[u].y, acc1[u].z, acc1[u].w};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) g[u][j] = accumulate1<ACC>(a, ac[j], g[u][j]);
-            }
-        }
-        // The block's kSqVecPerBlock * 32 bytes of the output (unused when
-        // it is not stored: then mean_out is null and nothing is written
-        // through it).
-        const __amdgpu_buffer_rsrc_t mr =
-            buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (STORE) {
-                const uint32_t off = static_cast<uint32_t>((u * BS + threadIdx.x) * 32);
-                buffer_store_f4<kSqNtStore>(mr, off, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
-                buffer_store_f4<kSqNtStore>(mr, off + 16, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const double d = g[u][j];
-                q = sq_add(q, d);
-            }
+    if (base + kSqVecPerBlock <= nfull) {
+        if constexpr (U == 1 && BS % 64 == 0) {
+            if (a.contiguous) reduce_block_contiguous<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
+            else reduce_block_plain<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
+        } else {
+            reduce_block_plain<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
         }
     } else {
         for (int u = 0; u < U; ++u) {
