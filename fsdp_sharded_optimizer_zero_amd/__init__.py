@@ -8,11 +8,14 @@ missing, importing the entry points raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
+# test build: at most 65,536 threads per launch (every entry point splits early)
+SMALLGRID_LIB_PATH = os.path.join(_HERE, "libzero_shard_smallgrid.so")
 
 ZS_OK = 0
 ZS_EINVAL_PSI = -1
@@ -66,42 +69,60 @@ class zs_reduce(C.Structure):
 _lib = None
 
 
+def _open(path: str):
+    """Load one build of the library and declare its entry points."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with __graft_entry__.build(); "
+                          "there is no CPU fallback")
+    L = C.CDLL(path)
+    P, vp, i32, i64, f64 = C.POINTER, C.c_void_p, C.c_int32, C.c_int64, C.c_double
+    L.zs_layout.argtypes = [i64, i32, i32, i64, i32, i32, P(zs_shard)]
+    L.zs_layout.restype = C.c_int
+    L.zs_workspace_bytes.argtypes = [P(zs_shard)]
+    L.zs_workspace_bytes.restype = C.c_size_t
+    L.zs_state_bytes.argtypes = [f64, i32, i32, f64]
+    L.zs_state_bytes.restype = f64
+    L.zs_comm_bytes.argtypes = [f64, i32, i32, f64]
+    L.zs_comm_bytes.restype = f64
+    L.shard_grad_sqnorm.argtypes = [P(zs_shard), vp, vp, vp, C.c_size_t, vp, i32, vp]
+    L.shard_grad_sqnorm.restype = C.c_int
+    L.zs_workspace_bytes_units.argtypes = [P(zs_shard), i32]
+    L.zs_workspace_bytes_units.restype = C.c_size_t
+    L.shard_grad_sqnorm_units.argtypes = [P(zs_shard), i32, vp, vp, vp, C.c_size_t, vp,
+                                          i32, vp]
+    L.shard_grad_sqnorm_units.restype = C.c_int
+    L.shard_grad_reduce.argtypes = [P(zs_shard), P(zs_reduce), vp, vp, vp, C.c_size_t,
+                                    vp, i32, vp]
+    L.shard_grad_reduce.restype = C.c_int
+    L.zero_shard_step.argtypes = [P(zs_shard), P(zs_adamw), vp, vp, vp, f64, vp, vp, vp,
+                                  vp, vp]
+    L.zero_shard_step.restype = C.c_int
+    L.shard_pack_gather.argtypes = [P(zs_shard), vp, vp, vp]
+    L.shard_pack_gather.restype = C.c_int
+    L.zs_strerror.argtypes = [C.c_int]
+    L.zs_strerror.restype = C.c_char_p
+    return L
+
+
 def lib():
     """Load libzero_shard.so; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build(); "
-                              "there is no CPU fallback")
-        L = C.CDLL(LIB_PATH)
-        P, vp, i32, i64, f64 = C.POINTER, C.c_void_p, C.c_int32, C.c_int64, C.c_double
-        L.zs_layout.argtypes = [i64, i32, i32, i64, i32, i32, P(zs_shard)]
-        L.zs_layout.restype = C.c_int
-        L.zs_workspace_bytes.argtypes = [P(zs_shard)]
-        L.zs_workspace_bytes.restype = C.c_size_t
-        L.zs_state_bytes.argtypes = [f64, i32, i32, f64]
-        L.zs_state_bytes.restype = f64
-        L.zs_comm_bytes.argtypes = [f64, i32, i32, f64]
-        L.zs_comm_bytes.restype = f64
-        L.shard_grad_sqnorm.argtypes = [P(zs_shard), vp, vp, vp, C.c_size_t, vp, i32, vp]
-        L.shard_grad_sqnorm.restype = C.c_int
-        L.zs_workspace_bytes_units.argtypes = [P(zs_shard), i32]
-        L.zs_workspace_bytes_units.restype = C.c_size_t
-        L.shard_grad_sqnorm_units.argtypes = [P(zs_shard), i32, vp, vp, vp, C.c_size_t, vp,
-                                              i32, vp]
-        L.shard_grad_sqnorm_units.restype = C.c_int
-        L.shard_grad_reduce.argtypes = [P(zs_shard), P(zs_reduce), vp, vp, vp, C.c_size_t,
-                                        vp, i32, vp]
-        L.shard_grad_reduce.restype = C.c_int
-        L.zero_shard_step.argtypes = [P(zs_shard), P(zs_adamw), vp, vp, vp, f64, vp, vp, vp,
-                                      vp, vp]
-        L.zero_shard_step.restype = C.c_int
-        L.shard_pack_gather.argtypes = [P(zs_shard), vp, vp, vp]
-        L.shard_pack_gather.restype = C.c_int
-        L.zs_strerror.argtypes = [C.c_int]
-        L.zs_strerror.restype = C.c_char_p
-        _lib = L
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Route every call of this module through another build of the same
+    ABI (the small-grid test build) while the context is open."""
+    global _lib
+    saved = lib()
+    _lib = _open(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def zs_strerror(code: int) -> str:

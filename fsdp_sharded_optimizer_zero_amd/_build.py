@@ -11,6 +11,10 @@ BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzero_shard.so")
 BENCH_LIB = os.path.join(PKG, "libzs_benchcopy.so")
+# The same library built with at most 65,536 threads per launch: a test build
+# that runs the multi-launch path of every entry point on small shards.
+SMALLGRID_LIB = os.path.join(PKG, "libzero_shard_smallgrid.so")
+SMALLGRID_THREADS = 65536
 
 # -ffp-contract=off: the step is defined with one rounding per operation.
 # -packed-fp32-ops off: no v_pk_* fp32 instructions are generated.
@@ -37,6 +41,12 @@ def build(verbose: bool = False) -> str:
     _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", host_o,
           kern_o], verbose)
     os.replace(LIB + ".tmp", LIB)
+    small_o = os.path.join(BUILD, "zs_kernels_smallgrid.o")
+    _run(["hipcc", *HIP_FLAGS, f"-DZS_MAX_LAUNCH_THREADS={SMALLGRID_THREADS}", "-c",
+          os.path.join(CSRC, "zs_kernels.hip"), "-o", small_o], verbose)
+    _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", SMALLGRID_LIB + ".tmp",
+          host_o, small_o], verbose)
+    os.replace(SMALLGRID_LIB + ".tmp", SMALLGRID_LIB)
     # bench-only copy kernel (not part of the ABI)
     _run(["hipcc", *HIP_FLAGS, "-shared", "-o", BENCH_LIB + ".tmp",
           os.path.join(CSRC, "zs_bench_copy.hip")], verbose)

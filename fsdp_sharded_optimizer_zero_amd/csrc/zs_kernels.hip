@@ -119,9 +119,18 @@ constexpr bool kSqNtLoad = ZS_SQ_NT_LOAD != 0;
 constexpr bool kSqNtStore = ZS_SQ_NT_STORE != 0;
 constexpr int64_t kStepVecPerBlock = static_cast<int64_t>(ZS_STEP_BS) * ZS_STEP_U;
 constexpr int kFinalThreads = 1024;
-// Blocks of one launch at most; a longer shard takes several launches
-// (2^24 blocks of 256 vectors of 8 cover 3.4e10 parameters).
-constexpr int64_t kMaxBlocksPerLaunch = int64_t(1) << 24;
+// Threads of one launch at most.  A dispatch counts its work-items in 32
+// bits, so a longer shard takes several launches, each with a grid below
+// that (2^31 threads of one 8-parameter vector cover 1.7e10 parameters).  A
+// test build lowers the limit to run the multi-launch path on small shards.
+#ifndef ZS_MAX_LAUNCH_THREADS
+#define ZS_MAX_LAUNCH_THREADS (int64_t(1) << 31)
+#endif
+constexpr int64_t kMaxLaunchThreads = ZS_MAX_LAUNCH_THREADS;
+static_assert(kMaxLaunchThreads >= 1024 && kMaxLaunchThreads < (int64_t(1) << 32),
+              "a launch holds at least one block of each kernel and fewer than 2^32 threads");
+// Blocks of `threads` threads in one launch at most.
+constexpr int64_t max_blocks(int threads) { return kMaxLaunchThreads / threads; }
 constexpr int kMaxDevices = 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -1021,8 +1030,9 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     (void)hipGetLastError();   // drop an error left by an unrelated earlier call
     hipStream_t st = static_cast<hipStream_t>(stream);
     double* partials = static_cast<double*>(workspace);
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    constexpr int64_t cap = max_blocks(kSqThreads);
+    for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
+        const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
         a.v0 = b0 * kSqVecPerBlock;
         a.partials = partials + b0;
         if ((rc = launch_sqnorm(a, mean_out != nullptr, nb, st)) != ZS_OK) return rc;
@@ -1066,8 +1076,9 @@ extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,
     for (int32_t u = 0; u < units; ++u) {
         fill_slices(s, reinterpret_cast<const void* const*>(grad_slices + u * s->n_d), &a.slices);
         a.mean_out = mean_out ? mean_out[u] : nullptr;
-        for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-            const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+        constexpr int64_t cap = max_blocks(kSqThreads);
+        for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
+            const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
             a.v0 = b0 * kSqVecPerBlock;
             a.partials = partials + static_cast<int64_t>(u) * blocks + b0;
             if ((rc = launch_sqnorm(a, a.mean_out != nullptr, nb, st)) != ZS_OK) return rc;
@@ -1127,8 +1138,9 @@ extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
     (void)hipGetLastError();
     hipStream_t st = static_cast<hipStream_t>(stream);
     double* partials = sqnorm_out ? static_cast<double*>(workspace) : nullptr;
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    constexpr int64_t cap = max_blocks(kSqThreads);
+    for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
+        const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
         a.v0 = b0 * kSqVecPerBlock;
         a.partials = partials ? partials + b0 : nullptr;
         rc = launch_reduce(a, r->grad_dtype == ZS_GRAD_F32, weighted, acc, nb, st);
@@ -1150,6 +1162,8 @@ extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,
     if ((grad_slices == nullptr) == (mean_in == nullptr)) return ZS_ENULL;
     const bool clip = h->max_grad_norm > 0.0;
     if (clip) {
+        // a sum of squares is never negative; NaN and +Inf propagate
+        if (other_sqnorm < 0.0) return ZS_EINVAL_HPARAM;
         if (!sqnorm) return ZS_ENULL;
         if ((reinterpret_cast<uintptr_t>(sqnorm) & 7u) != 0) return ZS_EALIGN;
     }
@@ -1184,8 +1198,9 @@ extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,
     a.c = make_consts(h);
     const int64_t blocks = ((s->shard_len >> 3) + kStepVecPerBlock - 1) / kStepVecPerBlock;
     (void)hipGetLastError();
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    constexpr int64_t cap = max_blocks(kStepThreads);
+    for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
+        const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
         a.v0 = b0 * kStepVecPerBlock;
         rc = launch_step(a, grad_slices != nullptr, clip, nb, static_cast<hipStream_t>(stream));
         if (rc != ZS_OK) return rc;
@@ -1203,8 +1218,9 @@ extern "C" int shard_pack_gather(const zs_shard* s, const float* master, uint16_
     if (!aligned16(param_out) || (master && !aligned16(master))) return ZS_EALIGN;
     const int64_t blocks = ((s->shard_len >> 3) + kStepThreads - 1) / kStepThreads;
     (void)hipGetLastError();
-    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocksPerLaunch) {
-        const int64_t nb = blocks - b0 < kMaxBlocksPerLaunch ? blocks - b0 : kMaxBlocksPerLaunch;
+    constexpr int64_t cap = max_blocks(kStepThreads);
+    for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
+        const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
         hipLaunchKernelGGL(k_pack, dim3(nb), dim3(kStepThreads), 0,
                            static_cast<hipStream_t>(stream), master, slot_base(s, param_out),
                            s->valid_len, s->shard_len, b0 * kStepThreads);

@@ -237,7 +237,8 @@ int shard_grad_reduce(const zs_shard* s, const zs_reduce* r, const void* const* 
  * If h->max_grad_norm > 0: `sqnorm` (device, one double, this shard's or the
  * accumulated squared norm) is required and the global squared norm is
  * Q = *sqnorm + other_sqnorm (other_sqnorm stands for the scalar all-reduce
- * of the other ranks' squared shard norms);
+ * of the other ranks' squared shard norms; a negative value is rejected with
+ * ZS_EINVAL_HPARAM, NaN and +Inf propagate as IEEE arithmetic does);
  * coef = f32(min(1, max_grad_norm / (sqrt(Q) + 1e-6))) in double, NaN kept,
  * and g = g * coef.  Otherwise `sqnorm` and other_sqnorm are ignored.
  * Then, for i < valid_len, in this order and in fp32 (b1 = f32(beta1),

@@ -97,9 +97,10 @@ FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
 MIS = FAKE + 2                 # misaligned
 
 
-def _step(s, h, slices=None, mean=None, sq=None, w=FAKE, m=FAKE, v=FAKE, out=FAKE):
+def _step(s, h, slices=None, mean=None, sq=None, w=FAKE, m=FAKE, v=FAKE, out=FAKE,
+          other=0.0):
     sl = None if slices is None else (C.c_void_p * len(slices))(*slices)
-    return Z.lib().zero_shard_step(C.byref(s), C.byref(h), sl, mean, sq, 0.0, w, m, v, out,
+    return Z.lib().zero_shard_step(C.byref(s), C.byref(h), sl, mean, sq, other, w, m, v, out,
                                    None)
 
 
@@ -137,6 +138,11 @@ def test_step_error_paths():
                dict(weight_decay=-0.1), dict(step=0), dict(lr=float("nan")),
                dict(max_grad_norm=float("inf"))):
         assert _step(s, Z.adamw(**kw), slices=sl, sq=FAKE) == Z.ZS_EINVAL_HPARAM, kw
+    # the other ranks' squared norm is a sum of squares (ignored without clip)
+    assert _step(s, h, slices=sl, sq=FAKE, other=-1e-300) == Z.ZS_EINVAL_HPARAM
+    assert _step(s, h, slices=sl, sq=FAKE, other=float("-inf")) == Z.ZS_EINVAL_HPARAM
+    h0 = Z.adamw(step=1, max_grad_norm=0.0)
+    assert _step(s, h0, slices=sl, other=-1.0, w=None) == Z.ZS_ENULL
     # both / neither gradient source; clip without the squared norm
     assert _step(s, h, slices=sl, mean=FAKE, sq=FAKE) == Z.ZS_ENULL
     assert _step(s, h, sq=FAKE) == Z.ZS_ENULL

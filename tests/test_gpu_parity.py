@@ -566,6 +566,10 @@ def test_gpu_error_paths_write_nothing():
             Z.zero_shard_step(shard, h, master=w, exp_avg=m, exp_avg_sq=v, param_out=out,
                               sqnorm=None, **kw)
         assert e.value.code == code
+    with pytest.raises(Z.ZSError) as e:     # a negative sum of squares from the other ranks
+        Z.zero_shard_step(s, Z.adamw(step=1, max_grad_norm=1.0), grad_slices=ptrs, sqnorm=sq,
+                          other_sqnorm=-1.0, master=w, exp_avg=m, exp_avg_sq=v, param_out=out)
+    assert e.value.code == Z.ZS_EINVAL_HPARAM
     torch.cuda.synchronize()
     assert bool((w == 1).all() and (m == 1).all() and (v == 1).all())
     assert bool((out == SENTINEL).all())
