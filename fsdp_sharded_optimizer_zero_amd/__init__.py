@@ -15,6 +15,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
 # test build: at most 65,536 threads per launch (every entry point splits early)
+# and the step's streaming loads at every size
 SMALLGRID_LIB_PATH = os.path.join(_HERE, "libzero_shard_smallgrid.so")
 
 ZS_OK = 0

@@ -11,10 +11,13 @@ BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzero_shard.so")
 BENCH_LIB = os.path.join(PKG, "libzs_benchcopy.so")
-# The same library built with at most 65,536 threads per launch: a test build
-# that runs the multi-launch path of every entry point on small shards.
+# The same library built with at most 65,536 threads per launch and the
+# step's streaming loads at every size: a test build that runs the
+# multi-launch path of every entry point, and the streaming step, on small
+# shards.
 SMALLGRID_LIB = os.path.join(PKG, "libzero_shard_smallgrid.so")
 SMALLGRID_THREADS = 65536
+SMALLGRID_DEFS = [f"-DZS_MAX_LAUNCH_THREADS={SMALLGRID_THREADS}", "-DZS_STEP_STREAM_BYTES=0"]
 
 # -ffp-contract=off: the step is defined with one rounding per operation.
 # -packed-fp32-ops off: no v_pk_* fp32 instructions are generated.
@@ -42,7 +45,7 @@ def build(verbose: bool = False) -> str:
           kern_o], verbose)
     os.replace(LIB + ".tmp", LIB)
     small_o = os.path.join(BUILD, "zs_kernels_smallgrid.o")
-    _run(["hipcc", *HIP_FLAGS, f"-DZS_MAX_LAUNCH_THREADS={SMALLGRID_THREADS}", "-c",
+    _run(["hipcc", *HIP_FLAGS, *SMALLGRID_DEFS, "-c",
           os.path.join(CSRC, "zs_kernels.hip"), "-o", small_o], verbose)
     _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", SMALLGRID_LIB + ".tmp",
           host_o, small_o], verbose)
