@@ -70,6 +70,10 @@ namespace {
 #ifndef ZS_SQ_WIDE_ND
 #define ZS_SQ_WIDE_ND 32
 #endif
+// Blocks per CU of the wide clip pass (fp32 slices, accumulation, N_d >= ZS_SQ_WIDE_ND).
+#ifndef ZS_SQ_WIDE_PER_CU
+#define ZS_SQ_WIDE_PER_CU 1
+#endif
 // Non-temporal (streaming) cache policy: stores of the step; loads and
 // stores of the clip pass.  Every byte here is touched once per pass.
 #ifndef ZS_STEP_NT_STORE
@@ -113,9 +117,15 @@ __device__ __forceinline__ int64_t block_span(int64_t b, int64_t nb, bool xcd_co
 // (2.93 -> 2.83 ms; accumulation passes 13.3 -> 13.0 ms for 4), slower by
 // ~1% for 64 bf16 slices, which keep the plain mapping.
 
-// Gradient slices whose loads one thread has in flight at once.
+// Gradient slices whose loads one thread has in flight at once; the wide
+// specializations (N_d >= ZS_SQ_WIDE_ND, one block per CU) keep fewer in
+// flight (64 slices of 1.09B: 24.04 vs 24.24 ms with 8, 24.75 with 3, 27.5
+// with 2; 8 slices: the same with 4 or 8).
 #ifndef ZS_RED_GROUP
 #define ZS_RED_GROUP 8
+#endif
+#ifndef ZS_RED_GROUP_WIDE
+#define ZS_RED_GROUP_WIDE 4
 #endif
 constexpr int kStepThreads = ZS_STEP_BS;
 constexpr int kStepU = ZS_STEP_U;
@@ -326,9 +336,9 @@ __device__ __forceinline__ void reduce_fetched(const Args& a, Fetch fetch, float
         if constexpr (WEIGHTED) g[k] = a.wt[0] * v[k];
         else g[k] = v[k];
     }
-    // Loads are issued ZS_RED_GROUP ranks at a time (bounded registers), the
-    // additions stay in rank order.
-    constexpr int G = ZS_RED_GROUP;
+    // Loads are issued G ranks at a time (bounded registers), the additions
+    // stay in rank order.
+    constexpr int G = NDT >= ZS_SQ_WIDE_ND ? ZS_RED_GROUP_WIDE : ZS_RED_GROUP;
     for (int r0 = 1; r0 < nd; r0 += G) {
         typename IO::Raw b[G];
 #pragma unroll
@@ -875,7 +885,7 @@ int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
     // bytes in flight at one block per CU
     const bool wide = std::is_same<GT, float>::value || ACC != kAccNone ||
                       a.n_d >= ZS_SQ_WIDE_ND;
-    const int per_cu = wide ? 1 : ZS_SQ_PER_CU;
+    const int per_cu = wide ? ZS_SQ_WIDE_PER_CU : ZS_SQ_PER_CU;
     const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>>(per_cu, &lds);
     if (rc != ZS_OK) return rc;
     hipLaunchKernelGGL((k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>), dim3(blocks),
