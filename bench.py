@@ -163,9 +163,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU's shard only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the multi-GPU exchange is not part of this build.",
-              flush=True)
+        print(f"bench.py times one GPU's shard step only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the exchange between GPUs is not implemented, so runs "
+              "on several GPUs are not supported.", flush=True)
         sys.exit(2)
 
     import torch
