@@ -36,8 +36,9 @@ def kernel_source_sha() -> str:
 
 def load_traffic(workload: str, kernel_prefix: str):
     """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE,
-    scaled by the plain copy's reading) from the committed counter summary of
-    this workload, if it was taken on the current kernel source; else None."""
+    scaled by the plain copy's reading, averaged over its dispatches) from the
+    committed counter summary of this workload, if it was taken on the current
+    kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -45,10 +46,12 @@ def load_traffic(workload: str, kernel_prefix: str):
         p = json.load(f)
     if p.get("kernel_src_sha") != kernel_source_sha():
         return None
-    hits = [k for k in p.get("kernels", {}) if k.startswith(kernel_prefix)]
+    hits = [v for k, v in p.get("kernels", {}).items() if k.startswith(kernel_prefix + "<")]
     if not hits:
         return None
-    return max(p["kernels"][k]["hbm_bytes_per_dispatch"] for k in hits)
+    # mean over the dispatches of every instantiation (micro-batch passes differ)
+    calls = [v.get("calls", 1) for v in hits]
+    return sum(v["hbm_bytes_per_dispatch"] * c for v, c in zip(hits, calls)) / sum(calls)
 
 
 def cpu_baseline(wl, shard, seconds: float):

@@ -37,18 +37,20 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     host_o = os.path.join(BUILD, "zs_host.o")
+    abi_o = os.path.join(BUILD, "zs_abi.o")
     kern_o = os.path.join(BUILD, "zs_kernels.o")
     _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "zs_host.cpp"), "-o", host_o], verbose)
+    _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "zs_abi.cpp"), "-o", abi_o], verbose)
     _run(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "zs_kernels.hip"), "-o", kern_o],
          verbose)
     _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", host_o,
-          kern_o], verbose)
+          abi_o, kern_o], verbose)
     os.replace(LIB + ".tmp", LIB)
     small_o = os.path.join(BUILD, "zs_kernels_smallgrid.o")
     _run(["hipcc", *HIP_FLAGS, *SMALLGRID_DEFS, "-c",
           os.path.join(CSRC, "zs_kernels.hip"), "-o", small_o], verbose)
     _run(["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", SMALLGRID_LIB + ".tmp",
-          host_o, small_o], verbose)
+          host_o, abi_o, small_o], verbose)
     os.replace(SMALLGRID_LIB + ".tmp", SMALLGRID_LIB)
     # bench-only copy kernel (not part of the ABI)
     _run(["hipcc", *HIP_FLAGS, "-shared", "-o", BENCH_LIB + ".tmp",

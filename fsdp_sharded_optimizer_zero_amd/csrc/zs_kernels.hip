@@ -1,5 +1,6 @@
-// zs_kernels.hip -- CDNA4 (gfx950) kernels of the sharded optimizer step and
-// the C-ABI entry points that validate arguments and launch them.
+// zs_kernels.hip -- CDNA4 (gfx950) kernels of the sharded optimizer step,
+// their launch shapes, and the enqueue_* functions through which the C-ABI
+// entry points (zs_abi.cpp) run them.
 //
 // Every kernel is a streaming, HBM-bound, elementwise pass (nothing here is
 // a contraction, so no MFMA): 64-lane waves, each lane owns 8 parameters and
@@ -195,51 +196,6 @@ __device__ __forceinline__ void buffer_store_f4(__amdgpu_buffer_rsrc_t r, uint32
                      __float_as_uint(v.w)};
     __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, NT ? kCachePolicyNt : 0);
 }
-
-struct SlicePtrs {
-    const void* p[ZS_MAX_RANKS];   // bf16 or fp32 rows, by the kernel's element type
-};
-
-struct StepArgs {
-    SlicePtrs slices;
-    const float* mean;
-    const double* sqnorm;
-    double other_sqnorm;
-    double max_norm;
-    float* w;
-    float* m;
-    float* v;
-    uint16_t* out;          // slot base: shard element 0
-    int64_t valid_len;
-    int64_t shard_len;
-    int64_t v0;             // first vector of this launch
-    int32_t n_d;
-    float nd;               // (float)n_d
-    float inv_nd;           // 1/n_d, exact when n_d is a power of two
-    StepConsts c;
-};
-
-struct SqArgs {
-    SlicePtrs slices;
-    float wt[ZS_MAX_RANKS]; // token weights (weighted reduction only)
-    float* mean_out;        // the reduced gradient; also read in place when
-                            // it is a micro-batch accumulator
-    double* partials;       // one per block of this launch; null: no norm
-    int64_t valid_len;
-    int64_t v0;             // first vector of this launch
-    int32_t n_d;
-    float nd;
-    float inv_nd;
-    float micro_count;      // m, the divisor of the last micro-batch
-    float inv_micro_count;  // 1/m when m is a power of two (exact), else 0
-    int32_t xcd_contiguous; // block-to-data mapping (see block_span)
-    int32_t contiguous;     // lane mapping of full blocks (see k_reduce_sqnorm)
-};
-
-// What the clip pass does with the accumulator: write the reduced slice
-// (no accumulation, or the first micro-batch), add it to the accumulator,
-// or add it and divide by the micro-batch count (the last micro-batch).
-enum AccMode { kAccNone = 0, kAccAdd = 1, kAccFinal = 2 };
 
 // ---- bf16 --------------------------------------------------------------------
 
@@ -823,8 +779,6 @@ __global__ void __launch_bounds__(kStepThreads)
 
 // ---- launch helpers -----------------------------------------------------------------
 
-bool is_pow2(int32_t n) { return n > 0 && (n & (n - 1)) == 0; }
-
 int launched()
 {
     return hipGetLastError() == hipSuccess ? ZS_OK : ZS_ELAUNCH;
@@ -1003,259 +957,73 @@ int launch_step(const StepArgs& a, bool from_slices, bool clip, bool stream, int
     }
 }
 
-int fill_slices(const zs_shard* s, const void* const* grad_slices, SlicePtrs* out)
-{
-    for (int r = 0; r < ZS_MAX_RANKS; ++r) out->p[r] = nullptr;
-    if (!grad_slices) return ZS_ENULL;
-    for (int r = 0; r < s->n_d; ++r) {
-        const void* p = grad_slices[r];
-        if (s->valid_len > 0) {
-            if (!p) return ZS_ENULL;
-            if (!aligned16(p)) return ZS_EALIGN;
-        }
-        out->p[r] = p;
-    }
-    return ZS_OK;
-}
-
-uint16_t* slot_base(const zs_shard* s, uint16_t* param_out)
-{
-    return s->out_mode == ZS_OUT_GATHER ? param_out + s->shard_offset : param_out;
-}
-
 }  // namespace
-}  // namespace zs
 
-using namespace zs;
+// ---- the passes, as the C-ABI entry points enqueue them -----------------------------
 
-extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices,
-                                 float* mean_out, void* workspace, size_t workspace_bytes,
-                                 double* sqnorm_out, int32_t accumulate, void* stream)
+int enqueue_reduce(SqArgs a, bool f32, bool weighted, int acc, bool store, double* partials,
+                   void* stream)
 {
-    int rc = check_shard(s);
-    if (rc != ZS_OK) return rc;
-    if (!workspace || !sqnorm_out) return ZS_ENULL;
-    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(sqnorm_out) & 7u) != 0)
-        return ZS_EALIGN;
-    if (mean_out && !aligned16(mean_out)) return ZS_EALIGN;
-    if (workspace_bytes < zs_workspace_bytes(s)) return ZS_EWORKSPACE;
-    SqArgs a;
-    rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &a.slices);
-    if (rc != ZS_OK) return rc;
-    a.mean_out = mean_out;
-    a.partials = static_cast<double*>(workspace);
-    a.valid_len = s->valid_len;
-    a.n_d = s->n_d;
-    a.nd = static_cast<float>(s->n_d);
-    a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
-    a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
-    a.contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 0 : 1;
-    a.micro_count = 1.0f;
-    a.inv_micro_count = 1.0f;
-    const int64_t blocks = sq_blocks(s->valid_len);
+    // block-to-data and lane mappings (see block_span and k_reduce_sqnorm)
+    a.xcd_contiguous = a.n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
+    a.contiguous = (f32 || a.n_d < ZS_SQ_WIDE_ND) ? 1 : 0;
+    const bool general = f32 || weighted || acc != kAccNone;
+    const int64_t blocks = sq_blocks(a.valid_len);
+    hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // drop an error left by an unrelated earlier call
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    double* partials = static_cast<double*>(workspace);
-    constexpr int64_t cap = max_blocks(kSqThreads);
-    for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
-        const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-        a.v0 = b0 * kSqVecPerBlock;
-        a.partials = partials + b0;
-        if ((rc = launch_sqnorm(a, mean_out != nullptr, nb, st)) != ZS_OK) return rc;
-    }
-    return launch_sqnorm_sums(partials, blocks, 1, sqnorm_out, accumulate, st);
-}
-
-extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,
-                                       const uint16_t* const* grad_slices,
-                                       float* const* mean_out, void* workspace,
-                                       size_t workspace_bytes, double* sqnorm_out,
-                                       int32_t accumulate, void* stream)
-{
-    int rc = check_shard(s);
-    if (rc != ZS_OK) return rc;
-    if (units < 1) return ZS_EINVAL_UNITS;
-    if (!grad_slices || !workspace || !sqnorm_out) return ZS_ENULL;
-    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(sqnorm_out) & 7u) != 0)
-        return ZS_EALIGN;
-    if (workspace_bytes < zs_workspace_bytes_units(s, units)) return ZS_EWORKSPACE;
-    // validate every unit before enqueueing anything
-    for (int32_t u = 0; u < units; ++u) {
-        SlicePtrs tmp;
-        rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices + u * s->n_d), &tmp);
-        if (rc != ZS_OK) return rc;
-        if (mean_out && mean_out[u] && !aligned16(mean_out[u])) return ZS_EALIGN;
-    }
-    SqArgs a;
-    a.valid_len = s->valid_len;
-    a.n_d = s->n_d;
-    a.nd = static_cast<float>(s->n_d);
-    a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
-    a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
-    a.contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 0 : 1;
-    a.micro_count = 1.0f;
-    a.inv_micro_count = 1.0f;
-    const int64_t blocks = sq_blocks(s->valid_len);
-    (void)hipGetLastError();
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    double* partials = static_cast<double*>(workspace);
-    for (int32_t u = 0; u < units; ++u) {
-        fill_slices(s, reinterpret_cast<const void* const*>(grad_slices + u * s->n_d), &a.slices);
-        a.mean_out = mean_out ? mean_out[u] : nullptr;
-        constexpr int64_t cap = max_blocks(kSqThreads);
-        for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
-            const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-            a.v0 = b0 * kSqVecPerBlock;
-            a.partials = partials + static_cast<int64_t>(u) * blocks + b0;
-            if ((rc = launch_sqnorm(a, a.mean_out != nullptr, nb, st)) != ZS_OK) return rc;
-        }
-    }
-    return launch_sqnorm_sums(partials, blocks, units, sqnorm_out, accumulate, st);
-}
-
-extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
-                                 const void* const* grad_slices, float* grad_out,
-                                 void* workspace, size_t workspace_bytes, double* sqnorm_out,
-                                 int32_t accumulate, void* stream)
-{
-    int rc = check_shard(s);
-    if (rc != ZS_OK) return rc;
-    if (!r) return ZS_ENULL;
-    if ((r->grad_dtype != ZS_GRAD_BF16 && r->grad_dtype != ZS_GRAD_F32) || r->reserved != 0 ||
-        r->micro_count < 1 || r->micro < 0 || r->micro >= r->micro_count)
-        return ZS_EINVAL_REDUCE;
-    if (s->valid_len > 0 && !grad_out) return ZS_ENULL;
-    if (grad_out && !aligned16(grad_out)) return ZS_EALIGN;
-    if (sqnorm_out) {
-        if (!workspace) return ZS_ENULL;
-        if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(sqnorm_out) & 7u) != 0)
-            return ZS_EALIGN;
-        if (workspace_bytes < zs_workspace_bytes(s)) return ZS_EWORKSPACE;
-    }
-    SqArgs a;
-    rc = fill_slices(s, grad_slices, &a.slices);
-    if (rc != ZS_OK) return rc;
-    const bool weighted = r->rank_tokens != nullptr;
-    for (int k = 0; k < ZS_MAX_RANKS; ++k) a.wt[k] = 0.0f;
-    if (weighted) {
-        // w_r = n_r / T in double, rounded once; T = 0 rejects the update.
-        double T = 0.0;
-        for (int k = 0; k < s->n_d; ++k) {
-            if (r->rank_tokens[k] < 0) return ZS_EINVAL_REDUCE;
-            T += static_cast<double>(r->rank_tokens[k]);
-        }
-        if (T == 0.0) return ZS_EZERO_TOKENS;
-        for (int k = 0; k < s->n_d; ++k)
-            a.wt[k] = static_cast<float>(static_cast<double>(r->rank_tokens[k]) / T);
-    }
-    const int acc = r->micro == 0 ? kAccNone
-                  : (r->micro == r->micro_count - 1 ? kAccFinal : kAccAdd);
-    a.mean_out = grad_out;
-    a.valid_len = s->valid_len;
-    a.n_d = s->n_d;
-    a.nd = static_cast<float>(s->n_d);
-    a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
-    a.xcd_contiguous = s->n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
-    a.contiguous = (r->grad_dtype == ZS_GRAD_F32 || s->n_d < ZS_SQ_WIDE_ND) ? 1 : 0;
-    a.micro_count = static_cast<float>(r->micro_count);
-    a.inv_micro_count = is_pow2(r->micro_count) ? 1.0f / static_cast<float>(r->micro_count)
-                                                : 0.0f;
-    const int64_t blocks = sq_blocks(s->valid_len);
-    (void)hipGetLastError();
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    double* partials = sqnorm_out ? static_cast<double*>(workspace) : nullptr;
     constexpr int64_t cap = max_blocks(kSqThreads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
         a.v0 = b0 * kSqVecPerBlock;
         a.partials = partials ? partials + b0 : nullptr;
-        rc = launch_reduce(a, r->grad_dtype == ZS_GRAD_F32, weighted, acc, nb, st);
+        const int rc = general ? launch_reduce(a, f32, weighted, acc, nb, st)
+                               : launch_sqnorm(a, store, nb, st);
         if (rc != ZS_OK) return rc;
     }
-    if (!sqnorm_out) return ZS_OK;
-    return launch_sqnorm_sums(partials, blocks, 1, sqnorm_out, accumulate, st);
+    return ZS_OK;
 }
 
-extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,
-                               const uint16_t* const* grad_slices, const float* mean_in,
-                               const double* sqnorm, double other_sqnorm, float* master,
-                               float* exp_avg, float* exp_avg_sq, uint16_t* param_out,
-                               void* stream)
+int enqueue_sqnorm_sums(double* partials, int64_t blocks, int32_t units, double* sqnorm_out,
+                        int accumulate, void* stream)
 {
-    int rc = check_shard(s);
-    if (rc != ZS_OK) return rc;
-    if ((rc = check_hparams(h)) != ZS_OK) return rc;
-    if ((grad_slices == nullptr) == (mean_in == nullptr)) return ZS_ENULL;
-    const bool clip = h->max_grad_norm > 0.0;
-    if (clip) {
-        // a sum of squares is never negative; NaN and +Inf propagate
-        if (other_sqnorm < 0.0) return ZS_EINVAL_HPARAM;
-        if (!sqnorm) return ZS_ENULL;
-        if ((reinterpret_cast<uintptr_t>(sqnorm) & 7u) != 0) return ZS_EALIGN;
-    }
-    if (!param_out) return ZS_ENULL;
-    if (!aligned16(param_out)) return ZS_EALIGN;
-    if (s->valid_len > 0) {
-        if (!master || !exp_avg || !exp_avg_sq) return ZS_ENULL;
-        if (!aligned16(master) || !aligned16(exp_avg) || !aligned16(exp_avg_sq))
-            return ZS_EALIGN;
-        if (mean_in && !aligned16(mean_in)) return ZS_EALIGN;
-    }
-    StepArgs a;
-    if (grad_slices) {
-        rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &a.slices);
-        if (rc != ZS_OK) return rc;
-    } else {
-        for (int r = 0; r < ZS_MAX_RANKS; ++r) a.slices.p[r] = nullptr;
-    }
-    a.mean = mean_in;
-    a.sqnorm = sqnorm;
-    a.other_sqnorm = other_sqnorm;
-    a.max_norm = h->max_grad_norm;
-    a.w = master;
-    a.m = exp_avg;
-    a.v = exp_avg_sq;
-    a.out = slot_base(s, param_out);
-    a.valid_len = s->valid_len;
-    a.shard_len = s->shard_len;
-    a.n_d = s->n_d;
-    a.nd = static_cast<float>(s->n_d);
-    a.inv_nd = is_pow2(s->n_d) ? 1.0f / static_cast<float>(s->n_d) : 0.0f;
-    a.c = make_consts(h);
-    const int64_t blocks = ((s->shard_len >> 3) + kStepVecPerBlock - 1) / kStepVecPerBlock;
+    return launch_sqnorm_sums(partials, blocks, units, sqnorm_out, accumulate,
+                              static_cast<hipStream_t>(stream));
+}
+
+int enqueue_step(StepArgs a, bool from_slices, bool clip, void* stream)
+{
+    const int64_t blocks = ((a.shard_len >> 3) + kStepVecPerBlock - 1) / kStepVecPerBlock;
     // bytes the whole step moves: gradient in, state in and out, bf16 out
     const int64_t step_bytes =
-        s->valid_len * (grad_slices ? 2 * static_cast<int64_t>(s->n_d) + 26 : 30);
+        a.valid_len * (from_slices ? 2 * static_cast<int64_t>(a.n_d) + 26 : 30);
     const bool stream_loads = step_bytes >= kStepStreamBytes;
+    hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     constexpr int64_t cap = max_blocks(kStepThreads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
         a.v0 = b0 * kStepVecPerBlock;
-        rc = launch_step(a, grad_slices != nullptr, clip, stream_loads, nb,
-                         static_cast<hipStream_t>(stream));
+        const int rc = launch_step(a, from_slices, clip, stream_loads, nb, st);
         if (rc != ZS_OK) return rc;
     }
     return ZS_OK;
 }
 
-extern "C" int shard_pack_gather(const zs_shard* s, const float* master, uint16_t* param_out,
-                                 void* stream)
+int enqueue_pack(const float* master, uint16_t* out, int64_t valid_len, int64_t shard_len,
+                 void* stream)
 {
-    int rc = check_shard(s);
-    if (rc != ZS_OK) return rc;
-    if (!param_out) return ZS_ENULL;
-    if (s->valid_len > 0 && !master) return ZS_ENULL;
-    if (!aligned16(param_out) || (master && !aligned16(master))) return ZS_EALIGN;
-    const int64_t blocks = ((s->shard_len >> 3) + kStepThreads - 1) / kStepThreads;
+    const int64_t blocks = ((shard_len >> 3) + kStepThreads - 1) / kStepThreads;
+    hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     constexpr int64_t cap = max_blocks(kStepThreads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-        hipLaunchKernelGGL(k_pack, dim3(nb), dim3(kStepThreads), 0,
-                           static_cast<hipStream_t>(stream), master, slot_base(s, param_out),
-                           s->valid_len, s->shard_len, b0 * kStepThreads);
-        if ((rc = launched()) != ZS_OK) return rc;
+        hipLaunchKernelGGL(k_pack, dim3(nb), dim3(kStepThreads), 0, st, master, out, valid_len,
+                           shard_len, b0 * kStepThreads);
+        const int rc = launched();
+        if (rc != ZS_OK) return rc;
     }
     return ZS_OK;
 }
+
+}  // namespace zs
