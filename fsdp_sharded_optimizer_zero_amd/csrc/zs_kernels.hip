@@ -80,10 +80,17 @@ namespace {
 #ifndef ZS_STEP_NT_STORE
 #define ZS_STEP_NT_STORE 1
 #endif
-// A step that moves at least this many bytes loads the reduced gradient and
-// v non-temporally (see k_step).
+// Lane mapping of the step's full blocks: 0 plain (a lane owns one vector of
+// 8 consecutive parameters), 1 contiguous (4 + 4 parameters 256 apart, as
+// in the clip pass; see step_block_contiguous).
+#ifndef ZS_STEP_CONTIG
+#define ZS_STEP_CONTIG 1
+#endif
+// A step that moves at least this many bytes -- twice the 256 MB Infinity
+// Cache, so that none of its operands can stay cached from one step to the
+// next -- loads the reduced gradient and v non-temporally (see k_step).
 #ifndef ZS_STEP_STREAM_BYTES
-#define ZS_STEP_STREAM_BYTES (int64_t(2) << 30)
+#define ZS_STEP_STREAM_BYTES (int64_t(512) << 20)
 #endif
 #ifndef ZS_SQ_NT_LOAD
 #define ZS_SQ_NT_LOAD 1
@@ -152,6 +159,7 @@ constexpr int kMaxDevices = 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <bool NT, typename T>
 __device__ __forceinline__ T load(const T* p)
@@ -440,7 +448,6 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
                 return typename SliceIO<float>::Raw{load<kSqNtLoad>(q4 + i0),
                                                     load<kSqNtLoad>(q4 + i1)};
             } else {
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                 const u32x2* q2 = static_cast<const u32x2*>(a.slices.p[r]);
                 const u32x2 lo = load<kSqNtLoad>(q2 + i0), hi = load<kSqNtLoad>(q2 + i1);
                 return u32x4{lo.x, lo.y, hi.x, hi.y};
@@ -634,6 +641,80 @@ __device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c,
 // vector stored as soon as it is computed: while vector u is computed, the
 // loads of vectors u+1.. are still in flight (software pipelining across the
 // thread's vectors).
+// AdamW on a lane's 8 parameters (clipped gradient when CLIP).
+template <bool CLIP, bool BC1_POW2, bool BC2_POW2>
+__device__ __forceinline__ void adamw8(const StepConsts& c, float coef, const float (&g)[8],
+                                       float (&W)[8], float (&M)[8], float (&V)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float gj = g[j];
+        if constexpr (CLIP) gj = gj * coef;
+        adamw1<BC1_POW2, BC2_POW2>(c, gj, W[j], M[j], V[j]);
+    }
+}
+
+// A full block of the step in the contiguous lane mapping: lane l of wave w
+// owns the parameters 4l..4l+3 and 256+4l..256+4l+3 of the wave's 512, i.e.
+// the f32x4 groups q0 and q1 = q0 + 64 of the fp32 arrays (and the 8-byte
+// groups q0, q1 of the bf16 ones), so every load and store instruction of a
+// wave covers one contiguous span.
+template <int BS, bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
+__device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t base)
+{
+    const int64_t q0 = 2 * base + (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
+    const int64_t q1 = q0 + 64;
+    const f32x4* w4 = reinterpret_cast<const f32x4*>(a.w);
+    const f32x4* m4 = reinterpret_cast<const f32x4*>(a.m);
+    const f32x4* v4 = reinterpret_cast<const f32x4*>(a.v);
+    float g[8];
+    if constexpr (FROM_SLICES) {
+        reduce_fetched<uint16_t, NDT, false>(
+            a,
+            [&](int r) {
+                const u32x2* p = static_cast<const u32x2*>(a.slices.p[r]);
+                const u32x2 lo = p[q0], hi = p[q1];
+                return u32x4{lo.x, lo.y, hi.x, hi.y};
+            },
+            g);
+    } else {
+        const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean);
+        const f32x4 x0 = load<STREAM>(g4 + q0), x1 = load<STREAM>(g4 + q1);
+        g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w;
+        g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
+    }
+    const f32x4 w0 = w4[q0], w1 = w4[q1], m0 = m4[q0], m1 = m4[q1];
+    const f32x4 v0 = load<STREAM>(v4 + q0), v1 = load<STREAM>(v4 + q1);
+    __builtin_amdgcn_sched_barrier(0);
+    float coef = 1.0f;
+    if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
+    __builtin_amdgcn_sched_barrier(0);
+    const StepConsts c = a.c;
+    float W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    if (c.bc1_pow2) {
+        if (c.bc2_pow2) adamw8<CLIP, true, true>(c, coef, g, W, M, V);
+        else adamw8<CLIP, true, false>(c, coef, g, W, M, V);
+    } else {
+        if (c.bc2_pow2) adamw8<CLIP, false, true>(c, coef, g, W, M, V);
+        else adamw8<CLIP, false, false>(c, coef, g, W, M, V);
+    }
+    constexpr bool NT = kStepNtStore;
+    f32x4* wo = reinterpret_cast<f32x4*>(a.w);
+    f32x4* mo = reinterpret_cast<f32x4*>(a.m);
+    f32x4* vo = reinterpret_cast<f32x4*>(a.v);
+    u32x2* oo = reinterpret_cast<u32x2*>(a.out);
+    store_f4<NT>(wo + q0, f32x4{W[0], W[1], W[2], W[3]});
+    store_f4<NT>(wo + q1, f32x4{W[4], W[5], W[6], W[7]});
+    store_f4<NT>(mo + q0, f32x4{M[0], M[1], M[2], M[3]});
+    store_f4<NT>(mo + q1, f32x4{M[4], M[5], M[6], M[7]});
+    store_f4<NT>(vo + q0, f32x4{V[0], V[1], V[2], V[3]});
+    store_f4<NT>(vo + q1, f32x4{V[4], V[5], V[6], V[7]});
+    store<NT>(oo + q0, u32x2{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3])});
+    store<NT>(oo + q1, u32x2{pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
+}
+
 template <int U, int BS, bool CLIP, bool BC1_POW2, bool BC2_POW2>
 __device__ __forceinline__ void adamw_store_vectors(const StepArgs& a, const StepConsts& c,
                                                     float coef, int64_t vi,
@@ -652,12 +733,7 @@ __device__ __forceinline__ void adamw_store_vectors(const StepArgs& a, const Ste
         float W[8] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w, w1[u].x, w1[u].y, w1[u].z, w1[u].w};
         float M[8] = {m0[u].x, m0[u].y, m0[u].z, m0[u].w, m1[u].x, m1[u].y, m1[u].z, m1[u].w};
         float V[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float gj = g[u][j];
-            if constexpr (CLIP) gj = gj * coef;
-            adamw1<BC1_POW2, BC2_POW2>(c, gj, W[j], M[j], V[j]);
-        }
+        adamw8<CLIP, BC1_POW2, BC2_POW2>(c, coef, g[u], W, M, V);
         const int64_t x = vi + u * BS;
         store_f4<NT>(w4 + 2 * x, f32x4{W[0], W[1], W[2], W[3]});
         store_f4<NT>(w4 + 2 * x + 1, f32x4{W[4], W[5], W[6], W[7]});
@@ -721,12 +797,16 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
 // slices, or the stored mean), clip, AdamW in place, bf16 cast into the
 // slot; vectors past valid_len are pads and get +0.  Block b of a launch
 // owns kStepVecPerBlock consecutive vectors.
-// STREAM: the stored gradient and v are loaded non-temporally.  Measured on
-// MI355X (interleaved medians): 4.53 vs 4.65 ms for 875M parameters, 5.71 vs
-// 5.86 ms for 1.09B; w or m non-temporal as well is slower (4.6-4.9 ms).  A
-// step whose operands fit the 256 MB Infinity Cache a few times over loses
-// (15.6M parameters: 79 vs 75 us), so the host picks STREAM from the bytes
-// the step moves.
+// Full blocks take the contiguous lane mapping (step_block_contiguous):
+// measured against the plain one on MI355X (interleaved medians, one box),
+// 4.40 vs 4.47 ms for 875M parameters, 5.33 vs 5.51 ms for 1.09B, 70 vs 75 us
+// for 15.6M.  The block that meets valid_len takes the plain path per vector.
+// STREAM: the stored gradient and v are loaded non-temporally: 4.40 vs 4.62
+// ms for 875M parameters, 5.65 vs 5.82 ms for 1.09B, 4.40 vs 4.55 ms for 32
+// calls of 27M; w or m non-temporal as well was slower.  A 15.6M-parameter
+// step, whose 467 MB of operands back-to-back steps find partly in the 256 MB
+// Infinity Cache, loses (74 vs 70 us), so the host picks STREAM from the
+// bytes the step moves (ZS_STEP_STREAM_BYTES).
 template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 __global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
 {
@@ -735,7 +815,10 @@ __global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
     const int64_t nslot = a.shard_len >> 3;
     const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kStepVecPerBlock;
     if (base + kStepVecPerBlock <= nfull) {
-        step_vectors<U, BS, FROM_SLICES, NDT, CLIP, STREAM>(a, base + threadIdx.x);
+        if constexpr (ZS_STEP_CONTIG && U == 1 && BS % 64 == 0)
+            step_block_contiguous<BS, FROM_SLICES, NDT, CLIP, STREAM>(a, base);
+        else
+            step_vectors<U, BS, FROM_SLICES, NDT, CLIP, STREAM>(a, base + threadIdx.x);
         return;
     }
     for (int u = 0; u < U; ++u) {
