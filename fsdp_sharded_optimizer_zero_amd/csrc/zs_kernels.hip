@@ -4,8 +4,8 @@
 //
 // Every kernel is a streaming, HBM-bound, elementwise pass (nothing here is
 // a contraction, so no MFMA): 64-lane waves, each lane owns 8 parameters and
-// moves every operand in 16-byte (or, for bf16 in the clip pass's
-// contiguous mapping, 8-byte) vector loads and stores.  Grids are one-shot:
+// moves every operand in 16-byte (or, for bf16 in the contiguous lane
+// mapping, 8-byte) vector loads and stores.  Grids are one-shot:
 // one thread per 8-parameter vector and hundreds of thousands of blocks,
 // dispatched in index order, so the addresses in flight form one window
 // that sweeps the arrays front to back (on MI355X a plain copy launched so
@@ -55,11 +55,12 @@ namespace {
 // a time (0: no cap).  A dynamic LDS reservation enforces the cap.  Few
 // resident waves keep the window of addresses in flight narrow, which suits
 // the HBM better than a full CU when 4 to 65 arrays stream at once.
-// Measured on MI355X: the step over an 875M-parameter shard is ~7% faster
-// at two 256-thread blocks per CU than uncapped (one block leaves its
-// division and square-root chain exposed); the clip pass is fastest at two
-// 512-thread blocks per CU over 8 bf16 slices, and at one for 64 slices,
-// for fp32 slices and for the accumulation passes (more loads per thread).
+// Measured on MI355X (875M-parameter shard): the step takes 4.41 ms at two
+// 256-thread blocks per CU, 5.08 at one (its division and square-root chain
+// exposed), 4.63 at three, 4.59 at one 512-thread block; ~7% more uncapped.
+// The clip pass is fastest at two 512-thread blocks per CU over 8 bf16
+// slices, and at one for 64 slices, for fp32 slices and for the
+// accumulation passes (more loads per thread).
 #ifndef ZS_STEP_PER_CU
 #define ZS_STEP_PER_CU 2
 #endif
@@ -75,8 +76,9 @@ namespace {
 #ifndef ZS_SQ_WIDE_PER_CU
 #define ZS_SQ_WIDE_PER_CU 1
 #endif
-// Non-temporal (streaming) cache policy: stores of the step; loads and
-// stores of the clip pass.  Every byte here is touched once per pass.
+// Non-temporal (streaming) cache policy: stores of the step (plain stores:
+// 4.72 vs 4.41 ms at 875M parameters); loads and stores of the clip pass.
+// Every byte here is touched once per pass.
 #ifndef ZS_STEP_NT_STORE
 #define ZS_STEP_NT_STORE 1
 #endif
