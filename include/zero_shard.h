@@ -25,14 +25,18 @@
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
- *    16-byte aligned, owned by the caller.  The library allocates nothing and
- *    keeps no state between calls.
+ *    16-byte aligned, owned by the caller.  The library allocates nothing.
+ *    The only state it keeps is, per device, the LDS size it queried and the
+ *    kernel attribute it set on first use (both set once, thread-safely);
+ *    calls may come from several host threads at once.
  *  - bf16 values are passed as their uint16_t bit patterns.
  *  - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue
  *    work and return; results are ready after the caller synchronises the
  *    stream.  A device fault surfaces at that synchronisation.
  *  - Arguments are validated on the host before anything is enqueued; a call
- *    that returns an error has enqueued nothing and written nothing.
+ *    that returns an error other than ZS_ELAUNCH has enqueued nothing and
+ *    written nothing.  ZS_ELAUNCH reports a launch the runtime refused; the
+ *    call's earlier launches (a long shard takes several) may have run.
  *  - Return value: ZS_OK (0) or one of the negative codes below.  Nothing is
  *    thrown across the ABI.
  *  - Arithmetic: IEEE-754 fp32, round to nearest even, no fused
