@@ -153,10 +153,13 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def _slices(grad_slices):
+def _slices(grad_slices, count: int):
+    """The host array of device pointers the C ABI reads `count` entries of."""
     if grad_slices is None:
         return None
-    arr = (C.c_void_p * len(grad_slices))(*[_ptr(g) for g in grad_slices])
+    if len(grad_slices) != count:
+        raise ValueError(f"{len(grad_slices)} gradient slice pointers given, {count} needed")
+    arr = (C.c_void_p * count)(*[_ptr(g) for g in grad_slices])
     return arr
 
 
@@ -193,7 +196,8 @@ def shard_grad_sqnorm(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
                            if hasattr(workspace, "numel") else zs_workspace_bytes(s))
-    _check(lib().shard_grad_sqnorm(C.byref(s), _slices(grad_slices), _ptr(mean_out),
+    _check(lib().shard_grad_sqnorm(C.byref(s), _slices(grad_slices, s.n_d),
+                                   _ptr(mean_out),
                                    _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
                                    1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm")
@@ -218,7 +222,8 @@ def shard_grad_sqnorm_units(s: zs_shard, grad_slices, mean_out, workspace, sqnor
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
                            if hasattr(workspace, "numel") else zs_workspace_bytes_units(s, units))
-    _check(lib().shard_grad_sqnorm_units(C.byref(s), units, _slices(grad_slices), means,
+    _check(lib().shard_grad_sqnorm_units(C.byref(s), units,
+                                         _slices(grad_slices, units * s.n_d), means,
                                          _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
                                          1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm_units")
@@ -242,7 +247,10 @@ def shard_grad_reduce(s: zs_shard, r: zs_reduce, grad_slices, grad_out, workspac
         workspace_bytes = (workspace.numel() * workspace.element_size()
                            if hasattr(workspace, "numel") else
                            (zs_workspace_bytes(s) if workspace is not None else 0))
-    _check(lib().shard_grad_reduce(C.byref(s), C.byref(r), _slices(grad_slices),
+    tokens = getattr(r, "_tokens", None)
+    if r.rank_tokens and (tokens is None or len(tokens) != s.n_d):
+        raise ValueError(f"rank_tokens must hold n_d = {s.n_d} counts")
+    _check(lib().shard_grad_reduce(C.byref(s), C.byref(r), _slices(grad_slices, s.n_d),
                                    _ptr(grad_out), _ptr(workspace), workspace_bytes,
                                    _ptr(sqnorm_out), 1 if accumulate else 0, _stream(stream)),
            "shard_grad_reduce")
@@ -251,7 +259,8 @@ def shard_grad_reduce(s: zs_shard, r: zs_reduce, grad_slices, grad_out, workspac
 def zero_shard_step(s: zs_shard, h: zs_adamw, grad_slices=None, mean_in=None, sqnorm=None,
                     other_sqnorm: float = 0.0, master=None, exp_avg=None, exp_avg_sq=None,
                     param_out=None, stream=None) -> None:
-    _check(lib().zero_shard_step(C.byref(s), C.byref(h), _slices(grad_slices), _ptr(mean_in),
+    _check(lib().zero_shard_step(C.byref(s), C.byref(h), _slices(grad_slices, s.n_d),
+                                 _ptr(mean_in),
                                  _ptr(sqnorm), float(other_sqnorm), _ptr(master),
                                  _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out),
                                  _stream(stream)), "zero_shard_step")

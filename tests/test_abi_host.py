@@ -252,3 +252,20 @@ def test_workspace_is_modest():
         wsb = Z.zs_workspace_bytes(s)
         assert 256 <= wsb <= max(256, s.valid_len * 4 // 256 + 256), (psi, wsb)
         assert wsb % 256 == 0
+
+
+def test_binding_checks_list_lengths():
+    """The binding refuses pointer and token lists whose length is not what
+    the C ABI will read (it would read past the host array)."""
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    with pytest.raises(ValueError):
+        Z.shard_grad_sqnorm(s, [FAKE] * 3, None, FAKE, FAKE, workspace_bytes=1 << 20)
+    with pytest.raises(ValueError):
+        Z.zero_shard_step(s, Z.adamw(step=1), grad_slices=[FAKE] * 5, master=FAKE, exp_avg=FAKE,
+                          exp_avg_sq=FAKE, param_out=FAKE)
+    with pytest.raises(ValueError):
+        Z.shard_grad_reduce(s, Z.make_reduce(rank_tokens=[1, 2, 3]), [FAKE] * 4, FAKE)
+    with pytest.raises(ValueError):
+        Z.shard_grad_reduce(s, Z.make_reduce(), [FAKE] * 2, FAKE)
+    with pytest.raises(ValueError):
+        Z.shard_grad_sqnorm_units(s, [FAKE] * 7, None, FAKE, FAKE, workspace_bytes=1 << 20)
