@@ -3,11 +3,14 @@ the library's calls) and replayed: every replay must equal the eager step bit
 for bit.  The step enqueues only kernels (no memset, no allocation, no host
 synchronisation), so it can be captured; the AdamW constants of step t are
 kernel arguments and are frozen at capture, so the eager reference repeats
-the same t.  Eager work and synchronisations run between the replays."""
-import numpy as np
+the same t.  Eager work and synchronisations run between the replays.  Both
+builds are captured: the normal one (one launch per pass, plain step loads at
+this size) and the small-grid test build (several launches per pass and the
+step's streaming loads)."""
 import pytest
 import torch
 
+import fsdp_sharded_optimizer_zero_amd as Z
 from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
 from zsgen.workloads import Workload
 
@@ -27,9 +30,17 @@ def _same(a, b):
                for x, y in zip(a, b))
 
 
+@pytest.mark.parametrize("build", ["normal", "smallgrid"])
 @pytest.mark.parametrize("micro", [1, 3])
-def test_captured_step_replays_equal_eager(micro):
-    wl = Workload(name="graph", psi=1_000_003, n_d=4, rank=3, align=8, stage=2,
+def test_captured_step_replays_equal_eager(micro, build):
+    path = Z.LIB_PATH if build == "normal" else Z.SMALLGRID_LIB_PATH
+    with Z.library(path):
+        _captured_step_replays_equal_eager(micro)
+
+
+def _captured_step_replays_equal_eager(micro):
+    # 1.3M parameters: 3 launches per pass in the small-grid build
+    wl = Workload(name="graph", psi=5_200_003, n_d=4, rank=3, align=8, stage=2,
                   out_mode="gather", m_sigma=1e-4, v_sigma=1e-6, lr=3e-4, weight_decay=0.1,
                   max_grad_norm=0.05, t0=7, steps=1, seed=12, micro_batches=micro)
     t = wl.t0
