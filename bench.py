@@ -123,8 +123,9 @@ def cpu_baseline(wl, shard, seconds: float):
 
 
 def copy_ceiling(torch, nbytes=4 << 30, reps=10):
-    """Practical HBM bandwidth of a plain 16-byte-vector copy (read+write),
-    launched one-shot (the launch shape that copies fastest on MI355X)."""
+    """Practical HBM bandwidth of a 16-byte-vector copy (read + write) with
+    non-temporal loads and stores, launched one-shot: the fastest copy
+    measured on MI355X."""
     import ctypes as C
     lib = C.CDLL(os.path.join(ROOT, "fsdp_sharded_optimizer_zero_amd", "libzs_benchcopy.so"))
     lib.zs_bench_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]

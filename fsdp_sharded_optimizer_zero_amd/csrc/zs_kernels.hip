@@ -90,7 +90,7 @@ namespace {
 #endif
 // A step that moves at least this many bytes -- twice the 256 MB Infinity
 // Cache, so that none of its operands can stay cached from one step to the
-// next -- loads the reduced gradient and v non-temporally (see k_step).
+// next -- loads all its operands non-temporally (see k_step).
 #ifndef ZS_STEP_STREAM_BYTES
 #define ZS_STEP_STREAM_BYTES (int64_t(512) << 20)
 #endif
@@ -675,7 +675,7 @@ __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t
             a,
             [&](int r) {
                 const u32x2* p = static_cast<const u32x2*>(a.slices.p[r]);
-                const u32x2 lo = p[q0], hi = p[q1];
+                const u32x2 lo = load<STREAM>(p + q0), hi = load<STREAM>(p + q1);
                 return u32x4{lo.x, lo.y, hi.x, hi.y};
             },
             g);
@@ -685,7 +685,8 @@ __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t
         g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w;
         g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
     }
-    const f32x4 w0 = w4[q0], w1 = w4[q1], m0 = m4[q0], m1 = m4[q1];
+    const f32x4 w0 = load<STREAM>(w4 + q0), w1 = load<STREAM>(w4 + q1);
+    const f32x4 m0 = load<STREAM>(m4 + q0), m1 = load<STREAM>(m4 + q1);
     const f32x4 v0 = load<STREAM>(v4 + q0), v1 = load<STREAM>(v4 + q1);
     __builtin_amdgcn_sched_barrier(0);
     float coef = 1.0f;
@@ -766,15 +767,15 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
     for (int u = 0; u < U; ++u) {
         const int64_t x = vi + u * BS;
         if constexpr (FROM_SLICES) {
-            reduce_vec<uint16_t, NDT>(a, x, g[u]);
+            reduce_vec<uint16_t, NDT, false, STREAM>(a, x, g[u]);
         } else {
             const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * x;
             const f32x4 x0 = load<STREAM>(g4), x1 = load<STREAM>(g4 + 1);
             g[u][0] = x0.x; g[u][1] = x0.y; g[u][2] = x0.z; g[u][3] = x0.w;
             g[u][4] = x1.x; g[u][5] = x1.y; g[u][6] = x1.z; g[u][7] = x1.w;
         }
-        w0[u] = w4[2 * x]; w1[u] = w4[2 * x + 1];
-        m0[u] = m4[2 * x]; m1[u] = m4[2 * x + 1];
+        w0[u] = load<STREAM>(w4 + 2 * x); w1[u] = load<STREAM>(w4 + 2 * x + 1);
+        m0[u] = load<STREAM>(m4 + 2 * x); m1[u] = load<STREAM>(m4 + 2 * x + 1);
         v0[u] = load<STREAM>(v4 + 2 * x); v1[u] = load<STREAM>(v4 + 2 * x + 1);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -803,12 +804,14 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
 // measured against the plain one on MI355X (interleaved medians, one box),
 // 4.40 vs 4.47 ms for 875M parameters, 5.33 vs 5.51 ms for 1.09B, 70 vs 75 us
 // for 15.6M.  The block that meets valid_len takes the plain path per vector.
-// STREAM: the stored gradient and v are loaded non-temporally: 4.40 vs 4.62
-// ms for 875M parameters, 5.65 vs 5.82 ms for 1.09B, 4.40 vs 4.55 ms for 32
-// calls of 27M; w or m non-temporal as well was slower.  A 15.6M-parameter
-// step, whose 467 MB of operands back-to-back steps find partly in the 256 MB
-// Infinity Cache, loses (74 vs 70 us), so the host picks STREAM from the
-// bytes the step moves (ZS_STEP_STREAM_BYTES).
+// STREAM: every operand is loaded non-temporally.  Measured with the
+// contiguous mapping (interleaved medians, one box): the stored gradient and
+// v non-temporal, 4.40 vs 4.62 ms for 875M parameters, 5.65 vs 5.82 ms for
+// 1.09B, 4.40 vs 4.55 ms for 32 calls of 27M; w and m as well, 4.32 vs 4.41,
+// 5.57 vs 5.65 and 4.18 vs 4.41 ms.  A 15.6M-parameter step, whose 467 MB of
+// operands back-to-back steps find partly in the 256 MB Infinity Cache,
+// loses (74 vs 70 us), so the host picks STREAM from the bytes the step
+// moves (ZS_STEP_STREAM_BYTES).
 template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 __global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
 {
