@@ -55,9 +55,10 @@ namespace {
 // a time (0: no cap).  A dynamic LDS reservation enforces the cap.  Few
 // resident waves keep the window of addresses in flight narrow, which suits
 // the HBM better than a full CU when 4 to 65 arrays stream at once.
-// Measured on MI355X (875M-parameter shard): the step takes 4.41 ms at two
-// 256-thread blocks per CU, 5.08 at one (its division and square-root chain
-// exposed), 4.63 at three, 4.59 at one 512-thread block; ~7% more uncapped.
+// Measured on MI355X (875M-parameter shard): the step takes 4.32 ms at two
+// 256-thread blocks per CU, 5.16 at one (its division and square-root chain
+// exposed), 4.54 at three; a copy of it without the arithmetic takes 4.32 at
+// its best residency, so the step runs at its access pattern's ceiling.
 // The clip pass is fastest at two 512-thread blocks per CU over 8 bf16
 // slices, and at one for 64 slices, for fp32 slices and for the
 // accumulation passes (more loads per thread).
