@@ -54,6 +54,20 @@ def load_traffic(workload: str, kernel_prefix: str):
     return sum(v["hbm_bytes_per_dispatch"] * c for v, c in zip(hits, calls)) / sum(calls)
 
 
+def host_cpu():
+    """The host processor the oracle ran on: model name and logical CPUs."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
 def cpu_baseline(wl, shard, seconds: float):
     """The oracle as it stands (single thread) on a bounded sample of the same
     shard: O1..O5 over consecutive 4M-parameter chunks until `seconds` of
@@ -115,6 +129,7 @@ def cpu_baseline(wl, shard, seconds: float):
     if m_count > 1:
         what += f", accumulated over {m_count} micro-batches"
     return {"value": done / spent / 1e9, "unit": "G params/s", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": (f"oracle O1-O5 ({what}, fp64 "
                        f"exact squared norm, clip, fp32 AdamW, bf16 pack) on the first {done:,} "
                        f"of the {V:,} shard parameters of workload {wl.name}, single "
