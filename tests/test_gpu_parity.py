@@ -8,6 +8,7 @@ whenever the clip coefficient cannot depend on the fp64 summation order, and
 is asserted then).  Run on an MI355X:  pytest -m gpu -s
 """
 import ctypes as C
+import zlib
 
 import numpy as np
 import pytest
@@ -573,3 +574,49 @@ def test_gpu_error_paths_write_nothing():
     torch.cuda.synchronize()
     assert bool((w == 1).all() and (m == 1).all() and (v == 1).all())
     assert bool((out == SENTINEL).all())
+
+
+# ---- degenerate hyperparameters --------------------------------------------------------
+
+DEGENERATE = [
+    ("lr 0: w unchanged", dict(lr=0.0)),
+    ("beta 0: m' = g, v' = g*g", dict(beta1=0.0, beta2=0.0)),
+    ("no weight decay", dict(weight_decay=0.0)),
+    ("t = 1 from zero moments", dict(step=1)),
+    ("large eps", dict(eps=1.0)),
+    ("beta near 1 at t = 1 (bias corrections ~1e-6)", dict(beta1=0.999999, beta2=0.9999999, step=1)),
+    ("t = 10^6: both bias corrections 1.0 (power of two)", dict(step=1_000_000)),
+    ("bc2 = 0.5: a power of two other than 1", dict(beta2=0.5, step=1)),
+    ("clip that never binds", dict(max_grad_norm=1e30)),
+    ("clip to 1e-38: clipped gradients subnormal", dict(max_grad_norm=1e-38)),
+]
+
+
+@pytest.mark.parametrize("name,kw", DEGENERATE, ids=[d[0] for d in DEGENERATE])
+def test_degenerate_hyperparameters(name, kw):
+    """Every schedule against the oracle on a ragged 5,000-parameter shard (two
+    full blocks of the step and a partial one), at hyperparameters where the
+    arithmetic degenerates."""
+    psi, n_d, rank = 4 * 5000 + 3, 4, 3
+    base = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=7,
+                max_grad_norm=0.0)
+    base.update(kw)
+    h = O.Hparams(**base)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    s = Z.zs_layout(psi, n_d, rank, 8, 2)
+    V = s.valid_len
+    slices = [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32)) for _ in range(n_d)]
+    w = rng.normal(0, 0.02, V).astype(np.float32)
+    zero_moments = base["step"] == 1
+    m = np.zeros(V, np.float32) if zero_moments else rng.normal(0, 1e-4, V).astype(np.float32)
+    v = (np.zeros(V, np.float32) if zero_moments else
+         np.abs(rng.normal(0, 1e-6, V)).astype(np.float32))
+    modes = ("mean", "reread") if h.max_grad_norm > 0 else ("slices",)
+    for mode in modes:
+        case = f"{name} / {mode}"
+        res = run_small_case(psi, n_d, rank, 8, 2, Z.ZS_OUT_GATHER, zs_h(h), slices, w, m, v,
+                             mode)
+        check_against_oracle(case, res[0], res, slices, w, m, v, h, 0.0, mode)
+        if base["lr"] == 0.0:
+            assert np.array_equal(res[1].view(np.uint32), w.view(np.uint32)), case
+    log(f"degenerate hyperparameters: {name}: bit-exact in {', '.join(modes)}")
