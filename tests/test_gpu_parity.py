@@ -611,7 +611,7 @@ def test_degenerate_hyperparameters(name, kw):
     m = np.zeros(V, np.float32) if zero_moments else rng.normal(0, 1e-4, V).astype(np.float32)
     v = (np.zeros(V, np.float32) if zero_moments else
          np.abs(rng.normal(0, 1e-6, V)).astype(np.float32))
-    modes = ("mean", "reread") if h.max_grad_norm > 0 else ("slices",)
+    modes = ("mean", "reread") if h.max_grad_norm > 0 else ("slices", "mean")
     for mode in modes:
         case = f"{name} / {mode}"
         res = run_small_case(psi, n_d, rank, 8, 2, Z.ZS_OUT_GATHER, zs_h(h), slices, w, m, v,
