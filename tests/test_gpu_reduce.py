@@ -225,3 +225,58 @@ def test_sqnorm_units_equals_per_unit_calls(n_d, units):
         acc.add(O.reduce_mean(sl))
     oq = acc.value() + 3.25
     assert abs(float(qb.item()) - oq) <= Q_REL_BAR * oq
+
+
+def _same_values(got, ref):
+    """Bit for bit on finite and infinite values; NaN matched as a class (a NaN
+    that an operation creates has a processor-dependent sign)."""
+    gn, rn = np.isnan(got), np.isnan(ref)
+    return (np.array_equal(gn, rn) and
+            np.array_equal(got[~gn].view(np.uint32), ref[~rn].view(np.uint32)))
+
+
+@pytest.mark.parametrize("f32,tokens,m", [(True, None, 1), (False, [3, 1, 0, 5], 1),
+                                          (False, None, 3), (True, [2, 2, 0, 1], 3)])
+def test_reduce_non_finite(f32, tokens, m):
+    """NaN and ±Inf in single ranks' slices through shard_grad_reduce (fp32
+    slices, token weights, accumulation): IEEE propagation as the oracle does
+    it, in full blocks and in the tail, including Inf + (-Inf) and a
+    zero-token rank holding an Inf (0 * Inf)."""
+    rng = np.random.default_rng(90 + m)
+    psi, n_d, rank = 4 * 3000 + 5, 4, 3
+    s = Z.zs_layout(psi, n_d, rank, 8, 2)
+    S, V = s.shard_len, s.valid_len
+    esize = 4 if f32 else 2
+    nan, inf = np.float32("nan"), np.float32("inf")
+    # (rank, index, value): idx 2 gets -Inf + Inf; idx 4 puts an Inf in rank 2
+    # (a zero-token rank where weighted); V - 1 sits in the tail
+    poison = [(0, 0, nan), (1, 5, inf), (2, 1000, -inf), (3, 1000, inf), (3, 2047, inf),
+              (1, 2047, inf), (2, 2048, inf), (0, V - 1, -inf)]
+    out = torch.from_numpy(np.full(V + GUARD, F32_SENTINEL, np.uint32).view(np.float32)).cuda()
+    ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
+    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    acc = np.empty(V, np.float32)
+    for j in range(m):
+        sl = _draw(rng, n_d, V, f32)
+        if j == m - 1:
+            for r, i, x in poison:
+                if f32:
+                    sl[r][i] = x
+                else:
+                    sl[r][i] = O.bf16_rne(np.array([x], np.float32))[0]
+        rows = _rows(sl, n_d, S, V, f32)
+        ptrs = [rows.data_ptr() + esize * S * r for r in range(n_d)]
+        last = j == m - 1
+        r = Z.make_reduce(Z.ZS_GRAD_F32 if f32 else Z.ZS_GRAD_BF16, j, m, tokens)
+        Z.shard_grad_reduce(s, r, ptrs, out, ws if last else None, sq if last else None)
+        torch.cuda.synchronize()
+        O.accumulate(_oracle_reduce(sl, tokens, f32), j, m, acc)
+        got = out.cpu().numpy()[:V]
+        case = f"f32={f32} tokens={tokens} j={j}/{m}"
+        assert _same_values(got, acc), case
+        assert np.all(out.cpu().numpy().view(np.uint32)[V:] == F32_SENTINEL), case
+        del rows
+    assert np.isnan(acc).sum() >= 2 and np.isinf(acc).any()
+    q = O.sqnorm(acc)
+    gq = float(sq.item())
+    assert np.isnan(q) and np.isnan(gq), (q, gq)
