@@ -620,3 +620,49 @@ def test_degenerate_hyperparameters(name, kw):
         if base["lr"] == 0.0:
             assert np.array_equal(res[1].view(np.uint32), w.view(np.uint32)), case
     log(f"degenerate hyperparameters: {name}: bit-exact in {', '.join(modes)}")
+
+
+def test_sixteen_byte_aligned_buffers():
+    """The ABI asks for 16-byte alignment only: every buffer 16 bytes past a
+    512-byte boundary (state, mean, slices, gather buffer, workspace) gives the
+    same bits as 512-byte-aligned buffers, on both step schedules."""
+    psi, n_d, rank = 4 * 9000 + 3, 4, 3
+    s = Z.zs_layout(psi, n_d, rank, 8, 2)
+    S, V = s.shard_len, s.valid_len
+    rng = np.random.default_rng(16)
+    slices = [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32)) for _ in range(n_d)]
+    w = rng.normal(0, 0.02, V).astype(np.float32)
+    m = rng.normal(0, 1e-4, V).astype(np.float32)
+    v = np.abs(rng.normal(0, 1e-6, V)).astype(np.float32)
+    h = Z.adamw(lr=3e-4, weight_decay=0.1, step=1000, max_grad_norm=0.05)
+
+    def run(shift):
+        """shift: bytes past the allocation's start (0 or 16)."""
+        def f32(x):
+            t = torch.zeros(x.size + 64, dtype=torch.float32, device="cuda")
+            t[shift // 4: shift // 4 + x.size] = torch.from_numpy(x).cuda()
+            return t[shift // 4:]
+        rows = torch.full((n_d * S + 64,), 0x7F80, dtype=torch.int16, device="cuda")
+        base = rows[shift // 2:]
+        for r in range(n_d):
+            base[r * S: r * S + V] = torch.from_numpy(slices[r].view(np.int16)).cuda()
+        ptrs = [base.data_ptr() + 2 * S * r for r in range(n_d)]
+        dw, dm, dv, mean = f32(w), f32(m), f32(v), f32(np.zeros(V, np.float32))
+        outbuf = torch.full((n_d * S + 64,), SENTINEL, dtype=torch.int16, device="cuda")
+        out = outbuf[shift // 2:]
+        wsb = torch.empty(Z.zs_workspace_bytes(s) // 8 + 8, dtype=torch.float64, device="cuda")
+        ws = wsb[shift // 8:]
+        sq = torch.zeros(2, dtype=torch.float64, device="cuda")
+        Z.shard_grad_sqnorm(s, ptrs, mean, ws, sq, workspace_bytes=Z.zs_workspace_bytes(s))
+        Z.zero_shard_step(s, h, mean_in=mean, sqnorm=sq, master=dw, exp_avg=dm, exp_avg_sq=dv,
+                          param_out=out)
+        Z.zero_shard_step(s, h, grad_slices=ptrs, sqnorm=sq, master=dw, exp_avg=dm,
+                          exp_avg_sq=dv, param_out=out)
+        torch.cuda.synchronize()
+        return [x[:V].cpu().numpy().view(np.uint32).copy() for x in (dw, dm, dv, mean)] + \
+               [out[:n_d * S].cpu().numpy().view(np.uint16).copy(), float(sq[0].item())]
+
+    aligned, shifted = run(0), run(16)
+    for name, a, b in zip(("w", "m", "v", "mean", "out"), aligned[:5], shifted[:5]):
+        assert np.array_equal(a, b), name
+    assert aligned[5] == shifted[5]
