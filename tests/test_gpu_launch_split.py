@@ -25,7 +25,7 @@ import fsdp_sharded_optimizer_zero_amd as Z
 import oracle as O
 from fsdp_sharded_optimizer_zero_amd._build import SMALLGRID_THREADS
 from parity_util import Q_REL_BAR, coef_is_robust, log
-from test_gpu_reduce import _run_case
+from reduce_util import run_reduce_case
 
 pytestmark = pytest.mark.gpu
 
@@ -196,4 +196,4 @@ def test_split_units():
 def test_split_reduce_modes(f32, tokens, m):
     """shard_grad_reduce: fp32 slices, token weights, micro-batch accumulation."""
     with Z.library(Z.SMALLGRID_LIB_PATH):
-        _run_case(4 * 1_100_000 - 9, 4, 3, f32, tokens, m, seed=31 + m)
+        run_reduce_case(4 * 1_100_000 - 9, 4, 3, f32, tokens, m, seed=31 + m)

@@ -18,70 +18,16 @@ from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
 from zsgen.workloads import NEXT, WORKLOADS
 from parity_util import (Q_REL_BAR, assert_bf16_close, assert_state_close, coef_is_robust,
                          log, oracle_sampled_step, oracle_sqnorm_chunked, sample_indices)
+from reduce_util import (F32_SENTINEL, GUARD, draw_slices, oracle_reduce, rows_on_device,
+                         run_reduce_case)
 
 pytestmark = pytest.mark.gpu
-
-GUARD = 64
-F32_SENTINEL = np.uint32(0x7FC00ABC)     # a NaN pattern the kernels never write
-
 
 @pytest.fixture(autouse=True)
 def _free_gpu_memory():
     yield
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
-
-
-def _rows(slices, n_d, S, V, f32):
-    """Device [n_d, S] rows; beyond V they hold +Inf the kernels must not read."""
-    if f32:
-        rows = torch.full((n_d, S), float("inf"), dtype=torch.float32)
-        for r in range(n_d):
-            rows[r, :V] = torch.from_numpy(slices[r][:V])
-    else:
-        rows = torch.full((n_d, S), 0x7F80, dtype=torch.int16)
-        for r in range(n_d):
-            rows[r, :V] = torch.from_numpy(slices[r][:V].view(np.int16))
-    return rows.cuda()
-
-
-def _oracle_reduce(slices, tokens, f32):
-    if tokens is not None:
-        return O.reduce_weighted(slices, O.token_weights(tokens))
-    return O.reduce_mean_f32(slices) if f32 else O.reduce_mean(slices)
-
-
-def _draw(rng, n_d, V, f32):
-    if f32:
-        return [rng.normal(0, 1e-3, V).astype(np.float32) for _ in range(n_d)]
-    return [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32)) for _ in range(n_d)]
-
-
-def _run_case(psi, n_d, rank, f32, tokens, m, seed):
-    rng = np.random.default_rng(seed)
-    s = Z.zs_layout(psi, n_d, rank, 8, 2)
-    S, V = s.shard_len, s.valid_len
-    esize = 4 if f32 else 2
-    out = torch.from_numpy(np.full(V + GUARD, F32_SENTINEL, np.uint32).view(np.float32)).cuda()
-    ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
-    sq = torch.zeros(1, dtype=torch.float64, device="cuda")
-    acc = np.empty(V, np.float32)
-    for j in range(m):
-        sl = _draw(rng, n_d, V, f32)
-        rows = _rows(sl, n_d, S, V, f32)
-        ptrs = [rows.data_ptr() + esize * S * r for r in range(n_d)]
-        last = j == m - 1
-        r = Z.make_reduce(Z.ZS_GRAD_F32 if f32 else Z.ZS_GRAD_BF16, j, m, tokens)
-        Z.shard_grad_reduce(s, r, ptrs, out, ws if last else None, sq if last else None)
-        torch.cuda.synchronize()
-        O.accumulate(_oracle_reduce(sl, tokens, f32), j, m, acc)
-        got = out.cpu().numpy().view(np.uint32)
-        case = f"psi={psi} n_d={n_d} k={rank} f32={f32} tokens={tokens} j={j}/{m}"
-        assert np.array_equal(got[:V], acc.view(np.uint32)), case
-        assert np.all(got[V:] == F32_SENTINEL), f"{case}: wrote past valid_len"
-        del rows
-    q = O.sqnorm(acc)
-    assert abs(float(sq.item()) - q) <= Q_REL_BAR * max(q, 1e-300), (psi, n_d, rank)
 
 
 def test_reduce_ragged_every_mode():
@@ -99,7 +45,7 @@ def test_reduce_ragged_every_mode():
                             if sum(tokens) == 0:
                                 tokens[0] = 1
                         for m in (1, 3):
-                            _run_case(psi, n_d, rank, f32, tokens, m, seed=n)
+                            run_reduce_case(psi, n_d, rank, f32, tokens, m, seed=n)
                             n += 1
     log(f"shard_grad_reduce: {n} ragged cases bit-exact")
 
@@ -109,8 +55,8 @@ def test_reduce_bf16_mean_is_the_sqnorm_path():
     rng = np.random.default_rng(31)
     s = Z.zs_layout(1_000_003, 8, 5, 8, 2)
     S, V = s.shard_len, s.valid_len
-    sl = _draw(rng, 8, V, False)
-    rows = _rows(sl, 8, S, V, False)
+    sl = draw_slices(rng, 8, V, False)
+    rows = rows_on_device(sl, 8, S, V, False)
     ptrs = [rows.data_ptr() + 2 * S * r for r in range(8)]
     a = torch.empty(V, dtype=torch.float32, device="cuda")
     b = torch.empty(V, dtype=torch.float32, device="cuda")
@@ -131,7 +77,7 @@ def test_reduce_token_worked_example_on_gpu():
     for f32 in (False, True):
         sl = ([np.full(V, 3.0, np.float32), np.full(V, 1.0, np.float32)] if f32 else
               [O.bf16_rne(np.full(V, 3.0, np.float32)), O.bf16_rne(np.full(V, 1.0, np.float32))])
-        rows = _rows(sl, 2, s.shard_len, V, f32)
+        rows = rows_on_device(sl, 2, s.shard_len, V, f32)
         es = 4 if f32 else 2
         ptrs = [rows.data_ptr(), rows.data_ptr() + es * s.shard_len]
         out = torch.zeros(V, dtype=torch.float32, device="cuda")
@@ -145,7 +91,7 @@ def test_reduce_zero_tokens_rejects_and_writes_nothing():
     rng = np.random.default_rng(32)
     s = Z.zs_layout(5000, 4, 2, 8, 2)
     S, V = s.shard_len, s.valid_len
-    rows = _rows(_draw(rng, 4, V, False), 4, S, V, False)
+    rows = rows_on_device(draw_slices(rng, 4, V, False), 4, S, V, False)
     ptrs = [rows.data_ptr() + 2 * S * r for r in range(4)]
     out = torch.full((V,), 7.0, dtype=torch.float32, device="cuda")
     with pytest.raises(Z.ZSError) as e:
@@ -200,7 +146,8 @@ def test_sqnorm_units_equals_per_unit_calls(n_d, units):
     psi = 300_007 if n_d < 64 else 40_009
     s = Z.zs_layout(psi, n_d, n_d - 1, 8, 3)
     S, V = s.shard_len, s.valid_len
-    rows = [_rows(_draw(rng, n_d, V, False), n_d, S, V, False) for _ in range(units)]
+    rows = [rows_on_device(draw_slices(rng, n_d, V, False), n_d, S, V, False)
+            for _ in range(units)]
     ptrs = [r.data_ptr() + 2 * S * k for r in rows for k in range(n_d)]
     means_a = [torch.empty(max(V, 8), dtype=torch.float32, device="cuda") for _ in range(units)]
     means_b = [torch.empty(max(V, 8), dtype=torch.float32, device="cuda") for _ in range(units)]
@@ -257,20 +204,20 @@ def test_reduce_non_finite(f32, tokens, m):
     sq = torch.zeros(1, dtype=torch.float64, device="cuda")
     acc = np.empty(V, np.float32)
     for j in range(m):
-        sl = _draw(rng, n_d, V, f32)
+        sl = draw_slices(rng, n_d, V, f32)
         if j == m - 1:
             for r, i, x in poison:
                 if f32:
                     sl[r][i] = x
                 else:
                     sl[r][i] = O.bf16_rne(np.array([x], np.float32))[0]
-        rows = _rows(sl, n_d, S, V, f32)
+        rows = rows_on_device(sl, n_d, S, V, f32)
         ptrs = [rows.data_ptr() + esize * S * r for r in range(n_d)]
         last = j == m - 1
         r = Z.make_reduce(Z.ZS_GRAD_F32 if f32 else Z.ZS_GRAD_BF16, j, m, tokens)
         Z.shard_grad_reduce(s, r, ptrs, out, ws if last else None, sq if last else None)
         torch.cuda.synchronize()
-        O.accumulate(_oracle_reduce(sl, tokens, f32), j, m, acc)
+        O.accumulate(oracle_reduce(sl, tokens, f32), j, m, acc)
         got = out.cpu().numpy()[:V]
         case = f"f32={f32} tokens={tokens} j={j}/{m}"
         assert _same_values(got, acc), case
