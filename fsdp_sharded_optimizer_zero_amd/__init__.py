@@ -102,6 +102,8 @@ def _open(path: str):
     L.shard_pack_gather.restype = C.c_int
     L.zs_strerror.argtypes = [C.c_int]
     L.zs_strerror.restype = C.c_char_p
+    L.zs_init.argtypes = []
+    L.zs_init.restype = C.c_int
     return L
 
 
@@ -164,6 +166,12 @@ def _slices(grad_slices, count: int):
 
 
 # ---- host calls ------------------------------------------------------------------
+
+def zs_init() -> None:
+    """Per-device set-up of the current device (before capturing library
+    calls into a HIP graph)."""
+    _check(lib().zs_init(), "zs_init")
+
 
 def zs_layout(psi: int, n_d: int, rank: int, align: int, stage: int = 2,
               out_mode: int = ZS_OUT_GATHER) -> zs_shard:

@@ -60,6 +60,28 @@ SqArgs reduce_args(const zs_shard* s, float* grad_out, int32_t micro_count)
 
 using namespace zs;
 
+namespace zs {
+namespace {
+
+// The clip pass of one shard into the partials workspace `partials`; the
+// shard, sqnorm_out and mean_out have been checked.
+int sqnorm_pass(const zs_shard* s, const uint16_t* const* grad_slices, float* mean_out,
+                double* partials, double* sqnorm_out, int32_t accumulate, void* stream)
+{
+    SqArgs a = reduce_args(s, mean_out, 1);
+    int rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &a.slices);
+    if (rc != ZS_OK) return rc;
+    rc = enqueue_reduce(a, false, false, kAccNone, mean_out != nullptr, partials, stream);
+    if (rc != ZS_OK) return rc;
+    return enqueue_sqnorm_sums(partials, sq_blocks(s->valid_len), 1, sqnorm_out, accumulate,
+                               stream);
+}
+
+}  // namespace
+}  // namespace zs
+
+extern "C" int zs_init(void) { return prepare_device(); }
+
 extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices,
                                  float* mean_out, void* workspace, size_t workspace_bytes,
                                  double* sqnorm_out, int32_t accumulate, void* stream)
@@ -70,14 +92,8 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
     if (!aligned16(workspace) || !aligned8(sqnorm_out)) return ZS_EALIGN;
     if (mean_out && !aligned16(mean_out)) return ZS_EALIGN;
     if (workspace_bytes < zs_workspace_bytes(s)) return ZS_EWORKSPACE;
-    SqArgs a = reduce_args(s, mean_out, 1);
-    rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &a.slices);
-    if (rc != ZS_OK) return rc;
-    double* partials = static_cast<double*>(workspace);
-    rc = enqueue_reduce(a, false, false, kAccNone, mean_out != nullptr, partials, stream);
-    if (rc != ZS_OK) return rc;
-    return enqueue_sqnorm_sums(partials, sq_blocks(s->valid_len), 1, sqnorm_out, accumulate,
-                               stream);
+    return sqnorm_pass(s, grad_slices, mean_out, static_cast<double*>(workspace), sqnorm_out,
+                       accumulate, stream);
 }
 
 extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,

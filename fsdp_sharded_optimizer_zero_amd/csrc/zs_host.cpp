@@ -171,7 +171,7 @@ const char* zs_strerror(int code)
     case ZS_ENULL: return "required pointer is NULL (or both/neither gradient source)";
     case ZS_EUNSUPPORTED: return "n_d exceeds ZS_MAX_RANKS";
     case ZS_EWORKSPACE: return "workspace smaller than zs_workspace_bytes";
-    case ZS_ELAUNCH: return "kernel launch failed";
+    case ZS_ELAUNCH: return "the HIP runtime refused a kernel launch or a set-up call";
     case ZS_EINVAL_REDUCE: return "invalid zs_reduce (dtype, micro-batch index/count or token count)";
     case ZS_EZERO_TOKENS: return "global token count is zero: the update is rejected";
     case ZS_EINVAL_UNITS: return "units must be at least 1";

@@ -110,6 +110,13 @@ int enqueue_step(StepArgs a, bool from_slices, bool clip, void* stream);
 int enqueue_pack(const float* master, uint16_t* out, int64_t valid_len, int64_t shard_len,
                  void* stream);
 
+// Per-device set-up (zs_kernels.hip), for the current device; each returns
+// ZS_OK or ZS_ELAUNCH.
+//   prepare_device: the set-up calls every kernel launch needs (the LDS
+//     query and the kernels' dynamic-LDS limits), so that later calls make
+//     none.
+int prepare_device();
+
 // Host-side checks; each returns ZS_OK or the error code to report.
 int check_shard(const zs_shard* s);
 int check_hparams(const zs_adamw* h);

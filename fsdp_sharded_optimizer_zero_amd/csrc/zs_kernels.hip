@@ -891,8 +891,10 @@ int device_lds_per_cu(int dev)
 
 // Dynamic LDS to request with each launch of kernel K so that at most
 // per_cu of its blocks fit on one CU (K itself uses < 1 KB of static LDS).
-// per_cu <= 0: no reservation.  Reservations above the default 64 KB per
-// block are enabled once per device with hipFuncSetAttribute.
+// per_cu <= 0: no reservation.  The first reservation above the default
+// 64 KB per block on a device raises K's limit there, once, to the most any
+// launch of K may ask for (one block per CU), because the residency of a
+// kernel that serves any N_d (NDT = 0) depends on the call's N_d.
 template <auto K>
 int lds_reservation(int per_cu, size_t* bytes)
 {
@@ -908,9 +910,10 @@ int lds_reservation(int per_cu, size_t* bytes)
         static std::atomic<uint64_t> enabled{0};
         const uint64_t bit = uint64_t(1) << dev;
         if ((enabled.load(std::memory_order_relaxed) & bit) == 0) {
+            const int64_t most = static_cast<int64_t>(lds_cu) / 1024 * 1024 - 1024;
             if (hipFuncSetAttribute(reinterpret_cast<const void*>(K),
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    static_cast<int>(b)) != hipSuccess)
+                                    static_cast<int>(most)) != hipSuccess)
                 return ZS_ELAUNCH;
             enabled.fetch_or(bit, std::memory_order_relaxed);
         }
@@ -918,6 +921,10 @@ int lds_reservation(int per_cu, size_t* bytes)
     *bytes = static_cast<size_t>(b);
     return ZS_OK;
 }
+
+// A launch helper called with blocks == kPrepareOnly launches nothing: it
+// only makes the per-device set-up calls its kernel needs (prepare_kernels).
+constexpr int64_t kPrepareOnly = 0;
 
 template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
 int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
@@ -930,7 +937,7 @@ int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
                       a.n_d >= ZS_SQ_WIDE_ND;
     const int per_cu = wide ? ZS_SQ_WIDE_PER_CU : ZS_SQ_PER_CU;
     const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>>(per_cu, &lds);
-    if (rc != ZS_OK) return rc;
+    if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
     hipLaunchKernelGGL((k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>), dim3(blocks),
                        dim3(kSqThreads), lds, st, a);
     return launched();
@@ -1014,7 +1021,7 @@ int launch_step_k(const StepArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
     const int rc = lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(ZS_STEP_PER_CU, &lds);
-    if (rc != ZS_OK) return rc;
+    if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
     hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, CLIP, STREAM>), dim3(blocks),
                        dim3(kStepThreads), lds, st, a);
     return launched();
@@ -1046,7 +1053,39 @@ int launch_step(const StepArgs& a, bool from_slices, bool clip, bool stream, int
     }
 }
 
+// Every kernel instantiation the launch helpers above can reach, prepared
+// for the current device without a launch (kPrepareOnly): all specialized
+// N_d, one power of two and one other N_d through each generic kernel, on
+// both sides of the wide clip pass's threshold.
+int prepare_kernels()
+{
+    static const int32_t nds[] = {1, 2, 4, 8, 16, 32, 64, 3, 48};
+    for (const int32_t nd : nds) {
+        StepArgs sa{};
+        sa.n_d = nd;
+        SqArgs qa{};
+        qa.n_d = nd;
+        for (int k = 0; k < 8; ++k) {
+            int rc = launch_step(sa, (k & 1) != 0, (k & 2) != 0, (k & 4) != 0, kPrepareOnly,
+                                 nullptr);
+            if (rc != ZS_OK) return rc;
+            if (k < 2 && (rc = launch_sqnorm(qa, k == 1, kPrepareOnly, nullptr)) != ZS_OK)
+                return rc;
+        }
+        for (int k = 0; k < 12; ++k) {
+            const int rc = launch_reduce(qa, (k & 1) != 0, (k & 2) != 0, k >> 2, kPrepareOnly,
+                                         nullptr);
+            if (rc != ZS_OK) return rc;
+        }
+    }
+    return ZS_OK;
+}
+
 }  // namespace
+
+// ---- per-device set-up ----------------------------------------------------------------
+
+int prepare_device() { return prepare_kernels(); }
 
 // ---- the passes, as the C-ABI entry points enqueue them -----------------------------
 

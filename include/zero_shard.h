@@ -25,10 +25,16 @@
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
- *    16-byte aligned, owned by the caller.  The library allocates nothing.
- *    The only state it keeps is, per device, the LDS size it queried and the
- *    kernel attribute it set on first use (both set once, thread-safely);
- *    calls may come from several host threads at once.
+ *    16-byte aligned, owned by the caller.  The library allocates nothing at
+ *    run time.  The only state it keeps is, per device, the LDS size it
+ *    queried and the kernels' dynamic-LDS limits it raised, both set once,
+ *    thread-safely, by zs_init or by the first call that needs them; calls
+ *    may come from several host threads at once.
+ *  - HIP graphs: every entry point enqueues kernels only (no memset, no
+ *    allocation, no synchronisation), so its calls may be captured into a
+ *    HIP graph.  The per-device set-up above is not a stream operation and
+ *    must not happen inside a capture: call zs_init on each device (or make
+ *    one call of each kind eagerly) before capturing.
  *  - bf16 values are passed as their uint16_t bit patterns.
  *  - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue
  *    work and return; results are ready after the caller synchronises the
@@ -73,7 +79,9 @@ extern "C" {
                                     neither of grad_slices and mean_in */
 #define ZS_EUNSUPPORTED   (-9)   /* n_d > ZS_MAX_RANKS */
 #define ZS_EWORKSPACE    (-10)   /* workspace smaller than zs_workspace_bytes */
-#define ZS_ELAUNCH       (-11)   /* the HIP runtime rejected a kernel launch */
+#define ZS_ELAUNCH       (-11)   /* the HIP runtime rejected a kernel launch
+                                    or a set-up call (device query, kernel
+                                    attribute) */
 #define ZS_EINVAL_REDUCE (-12)   /* zs_reduce: unknown grad_dtype, reserved != 0,
                                     micro outside [0, micro_count), micro_count
                                     < 1, or a negative token count */
@@ -115,7 +123,10 @@ typedef struct zs_adamw {
                               <= 0: no clip */
 } zs_adamw;
 
-/* Fill *out with the shard of `rank`.  The flat vector is padded at its tail
+/* Fill *out with the shard of `rank`.  "Data parallelism, ZeRO and FSDP",
+ * section 2 "What is redundant" (GPU k owns slice k of the parameters) and
+ * "How FSDP implements ZeRO-3" step 1 (FSDP1 cuts a unit's flat parameter
+ * into N_d equal chunks).  The flat vector is padded at its tail
  * to n_d*S with S = roundup(ceil(psi/n_d), align) (stage 0: S =
  * roundup(psi, align), offset 0, valid_len psi); slot k is [k*S, (k+1)*S).
  * Host only.  Errors: ZS_EINVAL_PSI/ND/RANK/LAYOUT(align < 1)/STAGE,
@@ -123,25 +134,38 @@ typedef struct zs_adamw {
 int zs_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align, int32_t stage,
               int32_t out_mode, zs_shard* out);
 
-/* Bytes of device workspace shard_grad_sqnorm needs: one fp64 partial sum
+/* Bytes of device workspace shard_grad_sqnorm needs for the squared norm of
+ * "Data parallelism, ZeRO and FSDP", section 7 "Common mistakes" (global
+ * clipping of sharded gradients): one fp64 partial sum
  * per block of its first pass (one block per 4096 parameters) plus one per
  * group of 4096 such partials, rounded up to 256 bytes -- 1.7 MB for an
  * 875M-parameter shard, at least 256 bytes (an empty shard).  Host only. */
 size_t zs_workspace_bytes(const zs_shard* s);
 
-/* Model-state bytes per GPU of the Theorem's table: weights and gradients
+/* Model-state bytes per GPU of the table of "Data parallelism, ZeRO and
+ * FSDP", section 3, Theorem "ZeRO memory and communication" (the same
+ * factors as state_bytes in "Distributed Training Basics -- DDP and FSDP",
+ * "Memory accounting", whose argument checks this follows): weights and gradients
  * 2 bytes each, K optimizer bytes per parameter.  stage 0: (4+K)psi,
  * 1: 4psi + K psi/n_d, 2: 2psi + (2+K) psi/n_d, 3: (4+K) psi/n_d.
  * Returns -1 for psi <= 0, n_d < 1 or an unknown stage.  Host only. */
 double zs_state_bytes(double psi, int32_t n_d, int32_t stage, double K);
 
-/* Bytes each GPU sends per step: 2psi elements for stages 0-2, 3psi for
+/* Bytes each GPU sends per step, from the elements column of the same
+ * Theorem ("Data parallelism, ZeRO and FSDP", section 3, proof items 5-7):
+ * 2psi elements for stages 0-2, 3psi for
  * stage 3, times bytes_per_elem and (n_d-1)/n_d (ring collectives).
  * Returns -1 on invalid arguments.  Host only. */
 double zs_comm_bytes(double psi, int32_t n_d, int32_t stage, double bytes_per_elem);
 
 /* Clip pass: the reduce-scatter's local reduction plus this shard's squared
- * L2 norm.
+ * L2 norm.  "Data parallelism, ZeRO and FSDP": section 2 "The communication
+ * is already there" (after the reduce-scatter GPU k holds slice k of the
+ * gradients) with the averaging of section 2 "Two GPUs, one batch" and the
+ * Proposition "DDP is exact" (the mean of the ranks' gradients; its order of
+ * summation changes only the last bits, hence the fixed rank order here);
+ * section 7 "Common mistakes" (a global clip over sharded gradients sums the
+ * squared shard norms, which this call provides for this shard).
  *   grad_slices  host array of n_d device pointers; grad_slices[r] is rank
  *                r's bf16 gradient for this shard, valid_len elements.
  *   mean_out     device fp32[valid_len] or NULL.  If given, receives
@@ -234,7 +258,15 @@ int shard_grad_reduce(const zs_shard* s, const zs_reduce* r, const void* const* 
                       float* grad_out, void* workspace, size_t workspace_bytes,
                       double* sqnorm_out, int32_t accumulate, void* stream);
 
-/* The fused optimizer step of this shard.  Exactly one gradient source:
+/* The fused optimizer step of this shard.  "Data parallelism, ZeRO and
+ * FSDP": section 2 "What is redundant" (AdamW is elementwise, so GPU k
+ * updates slice k from that slice's gradient, moments and fp32 master
+ * weights alone) and the table of "The communication is already there" (the
+ * update sits between the reduce-scatter and the all-gather of the new
+ * weights); section 3 Theorem (K = 12 bytes of fp32 master weight, m and v
+ * per parameter); section 5 "In code" (the AdamW expression order below);
+ * section 7 "Common mistakes" (the clip uses the global norm).  Exactly one
+ * gradient source:
  *   grad_slices  host array of n_d device pointers to bf16[valid_len]
  *                (reduced here, in rank order, as shard_grad_sqnorm does), or
  *   mean_in      device fp32[valid_len], the mean from shard_grad_sqnorm.
@@ -263,12 +295,21 @@ int zero_shard_step(const zs_shard* s, const zs_adamw* h, const uint16_t* const*
                     void* stream);
 
 /* Cast and pack only: param_out (placed as in zero_shard_step) receives
- * bf16_rne(master[i]) for i < valid_len and +0 in the pads.  The step of
+ * bf16_rne(master[i]) for i < valid_len and +0 in the pads.  "Data
+ * parallelism, ZeRO and FSDP", section 2 table (the all-gather of the new
+ * weights after the update) and section 3 Theorem (bf16 weights of 2 bytes
+ * next to the fp32 master copy); the slot layout of zs_layout.  The step of
  * the all-gather that needs no optimizer work (e.g. to publish weights after
  * loading a checkpoint).  Errors: ZS_ENULL, ZS_EINVAL_*, ZS_EALIGN,
  * ZS_ELAUNCH. */
 int shard_pack_gather(const zs_shard* s, const float* master, uint16_t* param_out,
                       void* stream);
+
+/* Per-device set-up for the current HIP device: queries its LDS size, raises
+ * the kernels' dynamic-LDS limits.  Optional; every entry point does what it needs itself on
+ * its first call on a device.  Call it on each device before capturing
+ * library calls into a HIP graph.  Returns ZS_OK or ZS_ELAUNCH. */
+int zs_init(void);
 
 /* Static description of an error code ("unknown error" otherwise). */
 const char* zs_strerror(int code);

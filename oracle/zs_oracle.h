@@ -109,9 +109,10 @@ void or_reduce_mean(int32_t n_d, const uint16_t* const* slices, int64_t n,
 void or_reduce_mean_f32in(int32_t n_d, const float* const* slices, int64_t n,
                           float* g_out);
 
-/* Token-weighted reduction.  [DPZ] §7 "Common mistakes": with a per-token
- * loss and a different number of tokens on each GPU, weight each GPU's
- * gradient by its token count.  [DDB] "DDP: replicated state, partitioned
+/* Token-weighted reduction.  [DPZ] §7 "Common mistakes", the item on sum
+ * versus mean and unequal token counts: when the loss is a mean over tokens
+ * and the ranks hold different numbers of tokens, the ranks' gradients are
+ * combined in proportion to those counts.  [DDB] "DDP: replicated state, partitioned
  * examples": ranks with 2 and 6 tokens and local mean losses 3 and 1 give
  * (2*3+6*1)/8 = 1.5, not 2; a zero-token rank contributes a zero and still
  * takes part; [DDB] "Practice and worked answers", item 4: if the global

@@ -7,6 +7,10 @@ the same t.  Eager work and synchronisations run between the replays.  Both
 builds are captured: the normal one (one launch per pass, plain step loads at
 this size) and the small-grid test build (several launches per pass and the
 step's streaming loads)."""
+import os
+import subprocess
+import sys
+
 import pytest
 import torch
 
@@ -83,3 +87,15 @@ def _captured_step_replays_equal_eager(micro):
         torch.cuda.synchronize()
         assert bool(torch.isfinite(junk))
         assert _same(_snapshot(eager), _snapshot(graphed)), f"replay {k} differs from eager"
+
+
+def test_capture_first_after_zs_init():
+    """A fresh process whose first library calls are captured, after zs_init
+    (which makes the per-device set-up calls that must stay out of a
+    capture): every replay equals the eager step."""
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "capture_first_child.py")
+    r = subprocess.run([sys.executable, "-u", child], capture_output=True, text=True,
+                       timeout=300)
+    print(r.stdout[-2000:], r.stderr[-2000:])
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "capture-first ok" in r.stdout

@@ -218,6 +218,31 @@ def test_stage0_ddp_equals_concatenated_shards():
     assert np.array_equal(cat_out, ddp[4][:psi])
 
 
+def test_generic_nd_across_the_residency_threshold():
+    """An N_d without a specialized kernel runs the generic one, whose clip
+    pass takes two blocks per CU below 32 slices and one from 32 up, with
+    twice the LDS reservation.  Both orders in one process: the larger
+    reservation after the smaller one on the same kernel, and back (the mean,
+    the token-weighted reduction and the step against the oracle)."""
+    from reduce_util import run_reduce_case
+    rng = np.random.default_rng(48)
+    for k, n_d in enumerate((3, 48, 5, 40)):
+        psi = n_d * 9000 + 5
+        rank = n_d - 1
+        s = Z.zs_layout(psi, n_d, rank, 8, 2)
+        V = s.valid_len
+        sl = [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32)) for _ in range(n_d)]
+        w = rng.normal(0, 0.02, V).astype(np.float32)
+        m = rng.normal(0, 1e-4, V).astype(np.float32)
+        v = np.abs(rng.normal(0, 1e-6, V)).astype(np.float32)
+        h = O.Hparams(lr=3e-4, weight_decay=0.1, step=3, max_grad_norm=0.05)
+        res = run_small_case(psi, n_d, rank, 8, 2, Z.ZS_OUT_GATHER, zs_h(h), sl, w, m, v, "mean")
+        check_against_oracle(("generic", n_d), res[0], res, sl, w, m, v, h, 0.0, "mean")
+        run_reduce_case(psi, n_d, rank, False, [(5 * r + 1) % 7 for r in range(n_d)], 1,
+                        seed=480 + k)
+    log("generic N_d 3, 48, 5, 40: bit-exact")
+
+
 # ---- workloads -------------------------------------------------------------------------
 
 def _compare_full(name, run, unit_data, wl, rank, steps):
