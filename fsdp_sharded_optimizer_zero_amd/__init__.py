@@ -33,6 +33,8 @@ ZS_ELAUNCH = -11
 ZS_EINVAL_REDUCE = -12
 ZS_EZERO_TOKENS = -13
 ZS_EINVAL_UNITS = -14
+ZS_ESCRATCH = -15
+ZS_SCRATCH_BYTES = 4 << 20
 ZS_GRAD_BF16 = 0
 ZS_GRAD_F32 = 1
 ZS_MAX_RANKS = 64
@@ -102,6 +104,8 @@ def _open(path: str):
     L.shard_pack_gather.restype = C.c_int
     L.zs_strerror.argtypes = [C.c_int]
     L.zs_strerror.restype = C.c_char_p
+    L.shard_grad_sqnorm_noalloc.argtypes = [P(zs_shard), vp, vp, vp, i32, vp]
+    L.shard_grad_sqnorm_noalloc.restype = C.c_int
     L.zs_init.argtypes = []
     L.zs_init.restype = C.c_int
     return L
@@ -209,6 +213,16 @@ def shard_grad_sqnorm(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
                                    _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
                                    1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm")
+
+
+def shard_grad_sqnorm_noalloc(s: zs_shard, grad_slices, mean_out, sqnorm_out,
+                              accumulate: bool = False, stream=None) -> None:
+    """shard_grad_sqnorm without a workspace argument: the library's static
+    per-device scratch array holds the block partials (no allocation)."""
+    _check(lib().shard_grad_sqnorm_noalloc(C.byref(s), _slices(grad_slices, s.n_d),
+                                           _ptr(mean_out), _ptr(sqnorm_out),
+                                           1 if accumulate else 0, _stream(stream)),
+           "shard_grad_sqnorm_noalloc")
 
 
 def zs_workspace_bytes_units(s: zs_shard, units: int) -> int:

@@ -96,6 +96,25 @@ extern "C" int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_
                        accumulate, stream);
 }
 
+extern "C" int shard_grad_sqnorm_noalloc(const zs_shard* s, const uint16_t* const* grad_slices,
+                                         float* mean_out, double* sqnorm_out,
+                                         int32_t accumulate, void* stream)
+{
+    int rc = check_shard(s);
+    if (rc != ZS_OK) return rc;
+    if (!sqnorm_out) return ZS_ENULL;
+    if (!aligned8(sqnorm_out)) return ZS_EALIGN;
+    if (mean_out && !aligned16(mean_out)) return ZS_EALIGN;
+    if (zs_workspace_bytes(s) > ZS_SCRATCH_BYTES) return ZS_ESCRATCH;
+    SqArgs tmp;
+    rc = fill_slices(s, reinterpret_cast<const void* const*>(grad_slices), &tmp.slices);
+    if (rc != ZS_OK) return rc;
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws)) != ZS_OK) return rc;
+    return sqnorm_pass(s, grad_slices, mean_out, static_cast<double*>(ws), sqnorm_out,
+                       accumulate, stream);
+}
+
 extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,
                                        const uint16_t* const* grad_slices,
                                        float* const* mean_out, void* workspace,

@@ -175,6 +175,7 @@ const char* zs_strerror(int code)
     case ZS_EINVAL_REDUCE: return "invalid zs_reduce (dtype, micro-batch index/count or token count)";
     case ZS_EZERO_TOKENS: return "global token count is zero: the update is rejected";
     case ZS_EINVAL_UNITS: return "units must be at least 1";
+    case ZS_ESCRATCH: return "shard too large for the static scratch array (ZS_SCRATCH_BYTES)";
     default: return "unknown error";
     }
 }

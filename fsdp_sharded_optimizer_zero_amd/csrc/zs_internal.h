@@ -113,9 +113,11 @@ int enqueue_pack(const float* master, uint16_t* out, int64_t valid_len, int64_t 
 // Per-device set-up (zs_kernels.hip), for the current device; each returns
 // ZS_OK or ZS_ELAUNCH.
 //   prepare_device: the set-up calls every kernel launch needs (the LDS
-//     query and the kernels' dynamic-LDS limits), so that later calls make
-//     none.
+//     query and the kernels' dynamic-LDS limits) and the address of the
+//     static scratch array, so that later calls make none.
+//   static_scratch: *ptr = this device's ZS_SCRATCH_BYTES scratch array.
 int prepare_device();
+int static_scratch(void** ptr);
 
 // Host-side checks; each returns ZS_OK or the error code to report.
 int check_shard(const zs_shard* s);

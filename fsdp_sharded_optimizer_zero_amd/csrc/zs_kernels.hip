@@ -39,6 +39,13 @@
 
 #include "zs_internal.h"
 
+// Workspace of the allocation-free clip pass (shard_grad_sqnorm_noalloc):
+// block partials and group sums, ZS_SCRATCH_BYTES in all.  Each device that
+// runs the library holds its own copy until the process ends.  Host code
+// reaches a device's copy only through the address static_scratch obtains
+// with hipGetSymbolAddress; the name itself is not a device address there.
+static __device__ __align__(256) double scratch[ZS_SCRATCH_BYTES / sizeof(double)];
+
 namespace zs {
 namespace {
 
@@ -1085,7 +1092,27 @@ int prepare_kernels()
 
 // ---- per-device set-up ----------------------------------------------------------------
 
-int prepare_device() { return prepare_kernels(); }
+int static_scratch(void** ptr)
+{
+    static std::atomic<void*> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ZS_ELAUNCH;
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ZS_ELAUNCH;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return ZS_OK;
+}
+
+int prepare_device()
+{
+    const int rc = prepare_kernels();
+    if (rc != ZS_OK) return rc;
+    void* p = nullptr;
+    return static_scratch(&p);
+}
 
 // ---- the passes, as the C-ABI entry points enqueue them -----------------------------
 

@@ -27,7 +27,8 @@
  *  - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
  *    16-byte aligned, owned by the caller.  The library allocates nothing at
  *    run time.  The only state it keeps is, per device, the LDS size it
- *    queried and the kernels' dynamic-LDS limits it raised, both set once,
+ *    queried, the kernels' dynamic-LDS limits it raised and the address of its
+ *    static scratch array (see shard_grad_sqnorm_noalloc), all set once,
  *    thread-safely, by zs_init or by the first call that needs them; calls
  *    may come from several host threads at once.
  *  - HIP graphs: every entry point enqueues kernels only (no memset, no
@@ -81,15 +82,20 @@ extern "C" {
 #define ZS_EWORKSPACE    (-10)   /* workspace smaller than zs_workspace_bytes */
 #define ZS_ELAUNCH       (-11)   /* the HIP runtime rejected a kernel launch
                                     or a set-up call (device query, kernel
-                                    attribute) */
+                                    attribute, symbol address) */
 #define ZS_EINVAL_REDUCE (-12)   /* zs_reduce: unknown grad_dtype, reserved != 0,
                                     micro outside [0, micro_count), micro_count
                                     < 1, or a negative token count */
 #define ZS_EZERO_TOKENS  (-13)   /* every rank_tokens entry is 0: the update is
                                     rejected on every rank; nothing is written */
 #define ZS_EINVAL_UNITS  (-14)   /* units < 1 */
+#define ZS_ESCRATCH      (-15)   /* shard_grad_sqnorm_noalloc: the shard needs
+                                    more than ZS_SCRATCH_BYTES of workspace */
 
 #define ZS_MAX_RANKS 64          /* gradient slices one call can reduce */
+/* Bytes of the per-device static scratch array of shard_grad_sqnorm_noalloc:
+ * the workspace of shards of up to 2,146,959,360 parameters. */
+#define ZS_SCRATCH_BYTES ((size_t)4 << 20)
 
 /* Where the new bf16 shard goes. */
 #define ZS_OUT_GATHER 0  /* param_out is the bf16[n_d * shard_len] all-gather
@@ -305,8 +311,28 @@ int zero_shard_step(const zs_shard* s, const zs_adamw* h, const uint16_t* const*
 int shard_pack_gather(const zs_shard* s, const float* master, uint16_t* param_out,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the clip
+ * pass of shard_grad_sqnorm with the same arguments except the workspace,
+ * computed by the same kernels into the same results bit for bit.  Its
+ * block partials live in a static device array of ZS_SCRATCH_BYTES (4 MiB)
+ * per device, held from the first use until the process ends; the call
+ * itself allocates nothing and needs no zeroed memory.  Every call on one
+ * device shares that device's array, so calls that overlap on one device
+ * (several streams or host threads at once) race and give wrong results;
+ * serialize them.  The array's device address is taken once per device by
+ * zs_init or by the first call on that device (outside a capture, see the
+ * HIP graph convention above).
+ * Errors: as shard_grad_sqnorm without ZS_EWORKSPACE, plus ZS_ESCRATCH when
+ * zs_workspace_bytes(s) > ZS_SCRATCH_BYTES (valid_len above
+ * 2,146,959,360); nothing is enqueued then. */
+int shard_grad_sqnorm_noalloc(const zs_shard* s, const uint16_t* const* grad_slices,
+                              float* mean_out, double* sqnorm_out, int32_t accumulate,
+                              void* stream);
+
 /* Per-device set-up for the current HIP device: queries its LDS size, raises
- * the kernels' dynamic-LDS limits.  Optional; every entry point does what it needs itself on
+ * the kernels' dynamic-LDS limits and takes the address of the static
+ * scratch array.  Optional; every entry point does what it needs itself on
  * its first call on a device.  Call it on each device before capturing
  * library calls into a HIP graph.  Returns ZS_OK or ZS_ELAUNCH. */
 int zs_init(void);

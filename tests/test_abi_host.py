@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_strerror_covers_codes():
-    for code in range(-14, 1):
+    for code in range(-15, 1):
         assert Z.zs_strerror(code) != "unknown error"
     assert Z.zs_strerror(-999) == "unknown error"
 
@@ -181,6 +181,32 @@ def test_sqnorm_and_pack_error_paths():
     assert L.shard_pack_gather(C.byref(s), None, FAKE, None) == Z.ZS_ENULL
     assert L.shard_pack_gather(C.byref(s), MIS, FAKE, None) == Z.ZS_EALIGN
     assert L.shard_pack_gather(C.byref(s), FAKE, MIS, None) == Z.ZS_EALIGN
+
+
+@no_gpu
+def test_sqnorm_noalloc_error_paths():
+    """The allocation-free clip pass checks as shard_grad_sqnorm does, and
+    rejects a shard whose workspace would not fit its static array."""
+    L = Z.lib()
+
+    def call(s, slices, mean=None, sq=FAKE):
+        arr = None if slices is None else (C.c_void_p * len(slices))(*slices)
+        return L.shard_grad_sqnorm_noalloc(C.byref(s), arr, mean, sq, 0, None)
+
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    assert call(s, None) == Z.ZS_ENULL
+    assert call(s, [FAKE] * 4, sq=None) == Z.ZS_ENULL
+    assert call(s, [FAKE] * 4, sq=FAKE + 4) == Z.ZS_EALIGN
+    assert call(s, [FAKE] * 4, mean=MIS) == Z.ZS_EALIGN
+    assert call(s, [FAKE, FAKE, MIS, FAKE]) == Z.ZS_EALIGN
+    # the largest shard whose workspace fits ZS_SCRATCH_BYTES, and one vector more
+    vmax = 2_146_959_360
+    ok = Z.zs_layout(vmax, 1, 0, 8, 0)
+    big = Z.zs_layout(vmax + 8, 1, 0, 8, 0)
+    assert Z.zs_workspace_bytes(ok) == Z.ZS_SCRATCH_BYTES
+    assert Z.zs_workspace_bytes(big) > Z.ZS_SCRATCH_BYTES
+    assert call(big, [FAKE]) == Z.ZS_ESCRATCH
+    assert "scratch" in Z.zs_strerror(Z.ZS_ESCRATCH)
 
 
 def _red(s, r, slices, out=FAKE, ws=None, wsb=None, sq=None):
