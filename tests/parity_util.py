@@ -2,8 +2,9 @@
 
 Every expected value here is computed by the CPU oracle (``oracle``) from
 inputs drawn by the HOST side of the seeded generator (``zsgen.host_*``);
-nothing here reads a value produced on the GPU.  The GPU side fills its own
-buffers with the device side of the same generator.
+no value produced on the GPU enters an expected value (compare_unit_full
+reads the device's results only to compare them).  The GPU side fills its
+own buffers with the device side of the same generator.
 """
 from __future__ import annotations
 
@@ -117,15 +118,19 @@ def oracle_full_run(wl: Workload, rank: int, steps: int, t0: int, shard, other_s
 
 
 def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
-                          chunk: int = 1 << 24, keep_idx=None, acc=None):
+                          chunk: int = 1 << 24, keep_idx=None, acc=None, keep_all=False):
     """Oracle squared norm of the mean over [start, start+n): the exact sum,
     accumulated chunk by chunk and rounded once.  The host generator fills
     chunk k+1 while the oracle reduces chunk k.  If keep_idx (sorted, relative
-    to start) is given, also returns the oracle's mean at those positions.
+    to start) is given, also returns the oracle's mean at those positions;
+    with keep_all, the oracle's whole gradient (fp32[n]) instead.
     Pass `acc` to keep accumulating into an existing exact accumulator (the
     global norm over several FSDP units)."""
     own = acc is None
     acc = O.SqAcc() if own else acc
+    if keep_all:
+        keep_idx = None
+        whole = np.empty(n, np.float32)
     kept = np.empty(0 if keep_idx is None else len(keep_idx), np.float32)
     starts = list(range(0, n, chunk))
 
@@ -141,15 +146,66 @@ def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
                 fut = ex.submit(gen, starts[ci + 1])
             g = oracle_gradient(wl, lambda j: sls[j])
             acc.add(g)
+            if keep_all:
+                whole[a:a + len(g)] = g
             if keep_idx is not None:
                 lo, hi = np.searchsorted(keep_idx, [a, a + len(g)])
                 kept[lo:hi] = g[keep_idx[lo:hi] - a]
             if ci % 8 == 7:
                 log(f"  oracle sqnorm {wl.name} unit {unit}: {a + len(g):,}/{n:,}")
     q = acc.value()
+    if keep_all:
+        return q, whole
     if keep_idx is not None:
         return q, kept
     return q
+
+
+def compare_unit_full(name, wl: Workload, run, unit: int, t: int, g, coef,
+                      chunk: int = 1 << 24):
+    """Every element of one unit's step against the oracle: chunk by chunk,
+    the oracle's AdamW (O4, with the oracle's clip coefficient `coef`, None
+    for no clip) and bf16 pack (O5) from the oracle's gradient `g` (fp32[V],
+    from oracle_sqnorm_chunked(keep_all=True)) and the host generator's
+    initial state, against the device's w, m, v, gather slot and stored
+    gradient.  Asserts the fp32 and bf16 bars on every element and returns
+    the number of elements that are not bit-identical (all arrays)."""
+    s = run.shard
+    d = run.units_data[unit]
+    V, off = s.valid_len, s.shard_offset
+    base = off if wl.out_mode == "gather" else 0
+    h = hparams(wl, t)
+    nbit = {"w": 0, "m": 0, "v": 0, "out": 0, "gradient": 0}
+    worst = {"w": 0.0, "m": 0.0, "v": 0.0}
+    max_ulp = 0
+    for a in range(0, V, chunk):
+        n = min(chunk, V - a)
+        w, m, v = host_state(wl, unit, off + a, n)
+        gc = g[a:a + n]
+        O.adamw_f32(h, gc, w, m, v, coef=coef)
+        ob = O.bf16_rne(w)
+        dev = {"w": d.w[a:a + n].cpu().numpy(), "m": d.m[a:a + n].cpu().numpy(),
+               "v": d.v[a:a + n].cpu().numpy()}
+        for k, ref in (("w", w), ("m", m), ("v", v)):
+            e = rel_err(dev[k], ref)
+            worst[k] = max(worst[k], float(e.max()))
+            assert e.max() <= REL_BAR, f"{name} {k}[{a}:{a + n}]: max rel err {e.max()}"
+            nbit[k] += int(np.count_nonzero(dev[k].view(np.uint32) != ref.view(np.uint32)))
+        gout = d.out[base + a:base + a + n].cpu().numpy().view(np.uint16)
+        dist = bf16_ulp_dist(gout, ob)
+        max_ulp = max(max_ulp, int(dist.max()))
+        assert dist.max() <= BF16_ULP_BAR, f"{name} out[{a}:{a + n}]: {dist.max()} ulp"
+        nbit["out"] += int(np.count_nonzero(gout != ob))
+        if d.mean is not None:
+            gm = d.mean[a:a + n].cpu().numpy()
+            nbit["gradient"] += int(np.count_nonzero(gm.view(np.uint32) != gc.view(np.uint32)))
+    for k in ("w", "m", "v"):
+        log(f"  {name} {k}: max rel err {worst[k]:.3g}, non-bitwise {nbit[k]:,}/{V:,}")
+    log(f"  {name} out: max bf16 ulp {max_ulp}, non-bitwise {nbit['out']:,}/{V:,}")
+    if d.mean is not None:
+        log(f"  {name} stored gradient: non-bitwise {nbit['gradient']:,}/{V:,}")
+        assert nbit["gradient"] == 0, f"{name}: stored gradient bits differ"
+    return sum(nbit.values())
 
 
 def oracle_sampled_step(wl: Workload, unit: int, t: int, shard, idx, coef):
