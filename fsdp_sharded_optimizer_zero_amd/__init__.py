@@ -141,13 +141,51 @@ def _check(rc: int, what: str) -> None:
         raise ZSError(rc, what)
 
 
-def _ptr(t):
-    """Device address of a tensor (or an int address, or None)."""
+_F32 = ("float32",)
+_F64 = ("float64",)
+_B16 = ("int16", "bfloat16", "uint16")      # bf16 bit patterns
+_ANY = None
+
+
+def _ptr(t, what: str = "buffer", dtypes=_ANY, min_numel: int = 0):
+    """Device address of a tensor, an int address, or None.
+
+    A torch tensor must have one of `dtypes` (torch dtype names; None: any),
+    be contiguous, hold at least `min_numel` elements (what the call reads or
+    writes through it) and live on the GPU; otherwise ValueError, before the
+    C ABI is called.  An int is passed through unchecked."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not hasattr(t, "data_ptr"):
+        raise TypeError(f"{what}: a torch tensor, an int device address or None is required")
+    name = str(t.dtype).replace("torch.", "")
+    if dtypes is not None and name not in dtypes:
+        raise ValueError(f"{what}: dtype {name}, expected {' or '.join(dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{what}: {t.numel()} elements, the call needs {min_numel}")
+    if not t.is_cuda:
+        raise ValueError(f"{what}: a GPU tensor is required (got {t.device})")
     return t.data_ptr()
+
+
+def _bytes_ptr(t, what: str, nbytes: int):
+    """As _ptr for a buffer of any dtype that must hold `nbytes` bytes."""
+    if t is not None and not isinstance(t, int) and hasattr(t, "numel"):
+        if t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{what}: {t.numel() * t.element_size()} bytes, the call needs "
+                             f"{nbytes}")
+    return _ptr(t, what)
+
+
+def _out_len(s: "zs_shard") -> int:
+    """Elements of param_out the step or the pack writes up to: the slot
+    [shard_offset, shard_offset + shard_len) of the gather buffer, or the
+    rank's own shard."""
+    return s.shard_len + (s.shard_offset if s.out_mode == ZS_OUT_GATHER else 0)
 
 
 def _stream(stream):
@@ -159,13 +197,15 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def _slices(grad_slices, count: int):
-    """The host array of device pointers the C ABI reads `count` entries of."""
+def _slices(grad_slices, count: int, valid_len: int = 0, dtypes=_B16):
+    """The host array of device pointers the C ABI reads `count` entries of
+    (each slice tensor must hold valid_len elements of `dtypes`)."""
     if grad_slices is None:
         return None
     if len(grad_slices) != count:
         raise ValueError(f"{len(grad_slices)} gradient slice pointers given, {count} needed")
-    arr = (C.c_void_p * count)(*[_ptr(g) for g in grad_slices])
+    arr = (C.c_void_p * count)(*[_ptr(g, f"grad_slices[{i}]", dtypes, valid_len)
+                                 for i, g in enumerate(grad_slices)])
     return arr
 
 
@@ -208,9 +248,11 @@ def shard_grad_sqnorm(s: zs_shard, grad_slices, mean_out, workspace, sqnorm_out,
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
                            if hasattr(workspace, "numel") else zs_workspace_bytes(s))
-    _check(lib().shard_grad_sqnorm(C.byref(s), _slices(grad_slices, s.n_d),
-                                   _ptr(mean_out),
-                                   _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
+    V = s.valid_len
+    _check(lib().shard_grad_sqnorm(C.byref(s), _slices(grad_slices, s.n_d, V),
+                                   _ptr(mean_out, "mean_out", _F32, V),
+                                   _bytes_ptr(workspace, "workspace", workspace_bytes),
+                                   workspace_bytes, _ptr(sqnorm_out, "sqnorm_out", _F64, 1),
                                    1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm")
 
@@ -219,8 +261,10 @@ def shard_grad_sqnorm_noalloc(s: zs_shard, grad_slices, mean_out, sqnorm_out,
                               accumulate: bool = False, stream=None) -> None:
     """shard_grad_sqnorm without a workspace argument: the library's static
     per-device scratch array holds the block partials (no allocation)."""
-    _check(lib().shard_grad_sqnorm_noalloc(C.byref(s), _slices(grad_slices, s.n_d),
-                                           _ptr(mean_out), _ptr(sqnorm_out),
+    V = s.valid_len
+    _check(lib().shard_grad_sqnorm_noalloc(C.byref(s), _slices(grad_slices, s.n_d, V),
+                                           _ptr(mean_out, "mean_out", _F32, V),
+                                           _ptr(sqnorm_out, "sqnorm_out", _F64, 1),
                                            1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm_noalloc")
 
@@ -240,13 +284,16 @@ def shard_grad_sqnorm_units(s: zs_shard, grad_slices, mean_out, workspace, sqnor
     if mean_out is not None:
         if len(mean_out) != units:
             raise ValueError("one mean buffer per unit")
-        means = (C.c_void_p * units)(*[_ptr(m) for m in mean_out])
+        means = (C.c_void_p * units)(*[_ptr(m, f"mean_out[{u}]", _F32, s.valid_len)
+                                       for u, m in enumerate(mean_out)])
     if workspace_bytes is None:
         workspace_bytes = (workspace.numel() * workspace.element_size()
                            if hasattr(workspace, "numel") else zs_workspace_bytes_units(s, units))
     _check(lib().shard_grad_sqnorm_units(C.byref(s), units,
-                                         _slices(grad_slices, units * s.n_d), means,
-                                         _ptr(workspace), workspace_bytes, _ptr(sqnorm_out),
+                                         _slices(grad_slices, units * s.n_d, s.valid_len),
+                                         means, _bytes_ptr(workspace, "workspace",
+                                                           workspace_bytes),
+                                         workspace_bytes, _ptr(sqnorm_out, "sqnorm_out", _F64, 1),
                                          1 if accumulate else 0, _stream(stream)),
            "shard_grad_sqnorm_units")
 
@@ -272,24 +319,33 @@ def shard_grad_reduce(s: zs_shard, r: zs_reduce, grad_slices, grad_out, workspac
     tokens = getattr(r, "_tokens", None)
     if r.rank_tokens and (tokens is None or len(tokens) != s.n_d):
         raise ValueError(f"rank_tokens must hold n_d = {s.n_d} counts")
-    _check(lib().shard_grad_reduce(C.byref(s), C.byref(r), _slices(grad_slices, s.n_d),
-                                   _ptr(grad_out), _ptr(workspace), workspace_bytes,
-                                   _ptr(sqnorm_out), 1 if accumulate else 0, _stream(stream)),
+    V = s.valid_len
+    gtypes = _F32 if r.grad_dtype == ZS_GRAD_F32 else _B16
+    _check(lib().shard_grad_reduce(C.byref(s), C.byref(r), _slices(grad_slices, s.n_d, V, gtypes),
+                                   _ptr(grad_out, "grad_out", _F32, V),
+                                   _bytes_ptr(workspace, "workspace", workspace_bytes),
+                                   workspace_bytes, _ptr(sqnorm_out, "sqnorm_out", _F64, 1),
+                                   1 if accumulate else 0, _stream(stream)),
            "shard_grad_reduce")
 
 
 def zero_shard_step(s: zs_shard, h: zs_adamw, grad_slices=None, mean_in=None, sqnorm=None,
                     other_sqnorm: float = 0.0, master=None, exp_avg=None, exp_avg_sq=None,
                     param_out=None, stream=None) -> None:
-    _check(lib().zero_shard_step(C.byref(s), C.byref(h), _slices(grad_slices, s.n_d),
-                                 _ptr(mean_in),
-                                 _ptr(sqnorm), float(other_sqnorm), _ptr(master),
-                                 _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(param_out),
+    V = s.valid_len
+    _check(lib().zero_shard_step(C.byref(s), C.byref(h), _slices(grad_slices, s.n_d, V),
+                                 _ptr(mean_in, "mean_in", _F32, V),
+                                 _ptr(sqnorm, "sqnorm", _F64, 1), float(other_sqnorm),
+                                 _ptr(master, "master", _F32, V),
+                                 _ptr(exp_avg, "exp_avg", _F32, V),
+                                 _ptr(exp_avg_sq, "exp_avg_sq", _F32, V),
+                                 _ptr(param_out, "param_out", _B16, _out_len(s)),
                                  _stream(stream)), "zero_shard_step")
 
 
 def shard_pack_gather(s: zs_shard, master, param_out, stream=None) -> None:
-    _check(lib().shard_pack_gather(C.byref(s), _ptr(master), _ptr(param_out),
+    _check(lib().shard_pack_gather(C.byref(s), _ptr(master, "master", _F32, s.valid_len),
+                                   _ptr(param_out, "param_out", _B16, _out_len(s)),
                                    _stream(stream)), "shard_pack_gather")
 
 

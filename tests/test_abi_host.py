@@ -295,3 +295,57 @@ def test_binding_checks_list_lengths():
         Z.shard_grad_reduce(s, Z.make_reduce(), [FAKE] * 2, FAKE)
     with pytest.raises(ValueError):
         Z.shard_grad_sqnorm_units(s, [FAKE] * 7, None, FAKE, FAKE, workspace_bytes=1 << 20)
+
+
+def test_binding_checks_tensors():
+    """Torch tensors handed to the binding are checked before the C ABI is
+    called: dtype, contiguity, the elements the call reads or writes through
+    them, and that they live on the GPU (int addresses are passed through)."""
+    s = Z.zs_layout(1000, 4, 1, 8, 2)
+    V, S, off = s.valid_len, s.shard_len, s.shard_offset
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)        # noqa: E731
+    b16 = lambda n: torch.zeros(n, dtype=torch.int16)          # noqa: E731
+    h = Z.adamw(step=1)
+
+    def step(**kw):
+        args = dict(grad_slices=[FAKE] * 4, master=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE,
+                    param_out=FAKE)
+        args.update(kw)
+        Z.zero_shard_step(s, h, **args)
+
+    with pytest.raises(ValueError, match="master: dtype float64"):
+        step(master=torch.zeros(V, dtype=torch.float64))
+    with pytest.raises(ValueError, match="exp_avg: the tensor must be contiguous"):
+        step(exp_avg=f32(2 * V)[::2])
+    with pytest.raises(ValueError, match=f"exp_avg_sq: {V - 1} elements, the call needs {V}"):
+        step(exp_avg_sq=f32(V - 1))
+    with pytest.raises(ValueError, match="master: a GPU tensor is required"):
+        step(master=f32(V))
+    with pytest.raises(ValueError, match=f"param_out: .* needs {off + S}"):
+        step(param_out=b16(off + S - 1))
+    with pytest.raises(ValueError, match="grad_slices\\[2\\]: dtype float32"):
+        step(grad_slices=[FAKE, FAKE, f32(V), FAKE])
+    with pytest.raises(ValueError, match="grad_slices\\[0\\]: a GPU tensor is required"):
+        step(grad_slices=[b16(V)] + [FAKE] * 3)
+    with pytest.raises(ValueError, match="mean_in: dtype int16"):
+        Z.zero_shard_step(s, h, mean_in=b16(V), master=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE,
+                          param_out=FAKE)
+    with pytest.raises(ValueError, match="sqnorm: dtype float32"):
+        step(sqnorm=f32(1))
+    wsb = Z.zs_workspace_bytes(s)
+    with pytest.raises(ValueError, match="workspace: .* bytes, the call needs"):
+        Z.shard_grad_sqnorm(s, [FAKE] * 4, None, torch.zeros(wsb // 8 - 1, dtype=torch.float64),
+                            FAKE, workspace_bytes=wsb)
+    with pytest.raises(ValueError, match=f"mean_out: {V - 1} elements"):
+        Z.shard_grad_sqnorm(s, [FAKE] * 4, f32(V - 1), FAKE, FAKE, workspace_bytes=wsb)
+    with pytest.raises(ValueError, match="grad_out: a GPU tensor"):
+        Z.shard_grad_reduce(s, Z.make_reduce(Z.ZS_GRAD_F32), [FAKE] * 4, f32(V))
+    with pytest.raises(ValueError, match="grad_slices\\[1\\]: dtype int16, expected float32"):
+        Z.shard_grad_reduce(s, Z.make_reduce(Z.ZS_GRAD_F32), [FAKE, b16(V), FAKE, FAKE], FAKE)
+    with pytest.raises(ValueError, match="master: a GPU tensor"):
+        Z.shard_pack_gather(s, f32(V), FAKE)
+    with pytest.raises(ValueError, match="sqnorm_out: dtype float32"):
+        Z.shard_grad_sqnorm_noalloc(s, [FAKE] * 4, None, f32(1))
+    with pytest.raises(ValueError, match="mean_out\\[1\\]: 3 elements"):
+        Z.shard_grad_sqnorm_units(s, [FAKE] * 8, [None, f32(3)], FAKE, FAKE,
+                                  workspace_bytes=1 << 20)
