@@ -137,14 +137,78 @@ def cpu_baseline(wl, shard, seconds: float):
             "seconds": spent}
 
 
-def copy_ceiling(torch, nbytes=4 << 30, reps=10):
-    """Practical HBM bandwidth of a 16-byte-vector copy (read + write) with
-    non-temporal loads and stores, launched one-shot: the fastest copy
-    measured on MI355X."""
+def bench_lib():
+    """The benchmark-only kernels (libzs_benchcopy.so, not part of the ABI)."""
     import ctypes as C
     lib = C.CDLL(os.path.join(ROOT, "fsdp_sharded_optimizer_zero_amd", "libzs_benchcopy.so"))
     lib.zs_bench_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_void_p]
     lib.zs_bench_copy.restype = C.c_int
+    lib.zs_bench_step_pattern.argtypes = [C.c_void_p] * 5 + [C.c_int64, C.c_int32, C.c_void_p]
+    lib.zs_bench_step_pattern.restype = C.c_int
+    return lib
+
+
+def step_pattern_ceiling(torch, run, reps=10):
+    """The step's access pattern without its arithmetic (k_step_pattern), on
+    the arrays of the workload's first unit: fp32 gradient, w, m, v in, w, m,
+    v and the bf16 slot out, over the first multiple of 2048 parameters, at
+    two and at one resident block per CU.  GB/s at 30 bytes per parameter.
+    Only for steps that read a stored fp32 gradient and stream (the pattern
+    of the dominant kernel there); runs after the timed region and leaves the
+    state changed."""
+    d = run.units_data[0]
+    n = run.V // 2048 * 2048
+    if d.mean is None or n == 0:
+        return None
+    lib = bench_lib()
+    out = d.out.data_ptr() + 2 * (run.shard.shard_offset if run.wl.out_mode == "gather" else 0)
+    st = torch.cuda.current_stream()
+    res = {}
+    for per_cu in (2, 1):
+        args = (d.mean.data_ptr(), d.w.data_ptr(), d.m.data_ptr(), d.v.data_ptr(), out, n,
+                per_cu, st.cuda_stream)
+        assert lib.zs_bench_step_pattern(*args) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            assert lib.zs_bench_step_pattern(*args) == 0
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[f"per_cu_{per_cu}"] = {"ms": ms, "gbps": 30 * n / (ms / 1e3) / 1e9}
+    best = max(res.values(), key=lambda r: r["gbps"])
+    return {"params": n, "gbps": best["gbps"], **res}
+
+
+def graph_replay(torch, run, t, steps):
+    """One whole step captured into a HIP graph (after zs_init) and replayed
+    `steps` times: the rate without host launch overhead, for steps short
+    enough that launches show.  The constants of step t are frozen at
+    capture."""
+    import fsdp_sharded_optimizer_zero_amd as Z
+    Z.zs_init()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.step(t)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"ms_per_step": ms, "value": run.V * run.units / (ms / 1e3) / 1e9,
+            "unit": "G params/s", "steps": steps}
+
+
+def copy_ceiling(torch, nbytes=4 << 30, reps=10):
+    """Practical HBM bandwidth of a 16-byte-vector copy (read + write) with
+    non-temporal loads and stores, launched one-shot: the fastest copy
+    measured on MI355X."""
+    lib = bench_lib()
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
@@ -223,8 +287,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    red_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    upd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    red_each = [e[0].elapsed_time(e[1]) for e in ev]
+    upd_each = [e[1].elapsed_time(e[2]) for e in ev]
+    red_ms = sum(red_each) / K
+    upd_ms = sum(upd_each) / K
     span_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
     ms_per_step = wall / K * 1e3
     params = run.V * run.units
@@ -248,6 +314,21 @@ def main():
     achieved = launch_bytes / (launch_ms / 1e3) / 1e9
     traffic = load_traffic(wl.name, "k_step" if kname.startswith("k_step") else
                            "k_reduce_sqnorm")
+    # the same figures as medians over windows of consecutive timed steps
+    # (run-to-run steadiness inside this process)
+    import statistics
+    W = 5 if K >= 10 else max(1, K)
+    wins = [(sum(red_each[i:i + W]) / W, sum(upd_each[i:i + W]) / W)
+            for i in range(0, K - W + 1, W)]
+    dom_idx = 1 if kname.startswith("k_step") else 0
+    dom_frac = [(launch_bytes * launches) / (w[dom_idx] / 1e3) / 1e9 / PEAK_HBM_GBPS
+                for w in wins]
+    whole_frac = [(red_b + upd_b) / ((w[0] + w[1]) / 1e3) / 1e9 / PEAK_HBM_GBPS for w in wins]
+    windows = {"steps_per_window": W, "windows": len(wins),
+               "dominant_kernel_frac_median": statistics.median(dom_frac),
+               "dominant_kernel_frac_min": min(dom_frac),
+               "dominant_kernel_frac_max": max(dom_frac),
+               "kernels_whole_step_frac_median": statistics.median(whole_frac)}
 
     out = {
         "metric": METRIC,
@@ -277,12 +358,26 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kname,
                      "algorithmic_bytes_per_launch": launch_bytes, "launch_ms": launch_ms,
                      "launches_per_step": launches},
+        "windows": windows,
         "kernel_src_sha": kernel_source_sha(),
     }
+    if ms_per_step < 1.0:
+        out["graph_replay"] = graph_replay(torch, run, t, K)
     if not args.no_copy_ceiling:
+        pattern = step_pattern_ceiling(torch, run) if (run.store_mean and kname.startswith(
+            "k_step") and launch_bytes >= (512 << 20)) else None
         del run
         torch.cuda.empty_cache()
-        out["copy_ceiling"] = copy_ceiling(torch)
+        cc = copy_ceiling(torch)
+        out["copy_ceiling"] = cc
+        ratios = {"dominant_kernel_over_copy": achieved / cc["gbps"],
+                  "kernels_whole_step_over_copy": (red_b + upd_b) / ((red_ms + upd_ms) / 1e3)
+                  / 1e9 / cc["gbps"]}
+        if pattern is not None:
+            out["step_pattern_ceiling"] = pattern
+            ratios["k_step_over_step_pattern"] = achieved / pattern["gbps"]
+            ratios["step_pattern_over_copy"] = pattern["gbps"] / cc["gbps"]
+        out["ceiling_ratios"] = ratios
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, Z.zs_layout(
             wl.psi, wl.n_d, wl.rank, wl.align, wl.stage,

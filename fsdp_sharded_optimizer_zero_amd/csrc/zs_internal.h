@@ -20,17 +20,11 @@ struct StepConsts {
     int32_t bc1_pow2, bc2_pow2;
 };
 
-// Launch shape of the clip pass (a build may override it): threads per
-// block, and 8-parameter vectors each thread reduces.  The pass writes one
-// fp64 partial sum per block into the workspace.
-#ifndef ZS_SQ_BS
-#define ZS_SQ_BS 512
-#endif
-#ifndef ZS_SQ_U
-#define ZS_SQ_U 1
-#endif
-constexpr int kSqThreads = ZS_SQ_BS;
-constexpr int64_t kSqVecPerBlock = static_cast<int64_t>(ZS_SQ_BS) * ZS_SQ_U;
+// Launch shape of the clip pass: threads per block, one 8-parameter vector
+// per thread.  The pass writes one fp64 partial sum per block into the
+// workspace.
+constexpr int kSqThreads = 512;
+constexpr int64_t kSqVecPerBlock = kSqThreads;
 
 // Blocks of the clip pass over valid_len parameters: one per kSqVecPerBlock
 // vectors of 8 (the last vector may be partial).
@@ -82,7 +76,6 @@ struct SqArgs {
     float micro_count;      // m, the divisor of the last micro-batch
     float inv_micro_count;  // 1/m when m is a power of two (exact), else 0
     int32_t xcd_contiguous; // block-to-data mapping (set by enqueue_reduce)
-    int32_t contiguous;     // lane mapping of full blocks (set by enqueue_reduce)
 };
 
 // What the clip pass does with the accumulator: write the reduced slice

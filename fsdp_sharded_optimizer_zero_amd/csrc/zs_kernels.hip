@@ -49,65 +49,59 @@ static __device__ __align__(256) double scratch[ZS_SCRATCH_BYTES / sizeof(double
 namespace zs {
 namespace {
 
-// Launch shape of the step and the pack (a build may override it): threads
-// per block and 8-parameter vectors per thread.  The clip pass's shape is in
-// zs_internal.h because the workspace size depends on it.
-#ifndef ZS_STEP_BS
-#define ZS_STEP_BS 256
-#endif
-#ifndef ZS_STEP_U
-#define ZS_STEP_U 1
-#endif
-// Blocks of the step / of the clip pass that may be resident on one CU at
-// a time (0: no cap).  A dynamic LDS reservation enforces the cap.  Few
-// resident waves keep the window of addresses in flight narrow, which suits
-// the HBM better than a full CU when 4 to 65 arrays stream at once.
-// Measured on MI355X (875M-parameter shard): the step takes 4.32 ms at two
-// 256-thread blocks per CU, 5.16 at one (its division and square-root chain
-// exposed), 4.54 at three; a copy of it without the arithmetic takes 4.32 at
-// its best residency, so the step runs at its access pattern's ceiling.
-// The clip pass is fastest at two 512-thread blocks per CU over 8 bf16
-// slices, and at one for 64 slices, for fp32 slices and for the
-// accumulation passes (more loads per thread).
-#ifndef ZS_STEP_PER_CU
-#define ZS_STEP_PER_CU 2
-#endif
-#ifndef ZS_SQ_PER_CU
-#define ZS_SQ_PER_CU 2
-#endif
+// ---- launch shapes and cache policies ---------------------------------------------
+//
+// Every choice below was measured on MI355X against its alternatives
+// (interleaved repeats in one process, the workloads' real sizes).
+//
+// Threads per block of the step and the pack; each thread owns one
+// 8-parameter vector.  The clip pass's shape is in zs_internal.h because the
+// workspace size depends on it.
+constexpr int kStepThreads = 256;
+constexpr int64_t kStepVecPerBlock = kStepThreads;
+// Blocks of the step / of the clip pass that may be resident on one CU at a
+// time.  A dynamic LDS reservation enforces the cap.  Few resident waves keep
+// the window of addresses in flight narrow, which suits the HBM better than a
+// full CU when 4 to 65 arrays stream at once.  The step takes 4.39 ms on an
+// 872M-parameter shard at two 256-thread blocks per CU, 5.10 at one (its
+// division and square-root chain exposed), 4.60 at three, 4.84 uncapped;
+// 512-thread blocks at one per CU, or 2 or 4 vectors per thread, 4.62-4.83.
+// The clip pass is fastest at two 512-thread blocks per CU over 8 bf16 slices,
+// and at one for 64 slices, for fp32 slices and for the accumulation passes
+// (more loads per thread).
+constexpr int kStepPerCu = 2;
+constexpr int kSqPerCu = 2;
 // The clip pass with this many slices or more keeps enough loads in flight
-// per thread to run at one block per CU.
-#ifndef ZS_SQ_WIDE_ND
-#define ZS_SQ_WIDE_ND 32
-#endif
-// Blocks per CU of the wide clip pass (fp32 slices, accumulation, N_d >= ZS_SQ_WIDE_ND).
-#ifndef ZS_SQ_WIDE_PER_CU
-#define ZS_SQ_WIDE_PER_CU 1
-#endif
-// Non-temporal (streaming) cache policy: stores of the step (plain stores:
-// 4.72 vs 4.41 ms at 875M parameters); loads and stores of the clip pass.
-// Every byte here is touched once per pass.
-#ifndef ZS_STEP_NT_STORE
-#define ZS_STEP_NT_STORE 1
-#endif
-// Lane mapping of the step's full blocks: 0 plain (a lane owns one vector of
-// 8 consecutive parameters), 1 contiguous (4 + 4 parameters 256 apart, as
-// in the clip pass; see step_block_contiguous).
-#ifndef ZS_STEP_CONTIG
-#define ZS_STEP_CONTIG 1
-#endif
+// per thread to run at one block per CU; fp32 slices and accumulation passes
+// run there too.
+constexpr int kSqWideNd = 32;
+constexpr int kSqWidePerCu = 1;
+// Gradient slices whose loads one thread has in flight at once; the wide
+// specializations (N_d >= kSqWideNd, one block per CU) keep fewer in flight
+// (64 slices of 1.09B: 24.04 vs 24.24 ms with 8, 24.75 with 3, 27.5 with 2;
+// 8 slices: the same with 4 or 8).
+constexpr int kRedGroup = 8;
+constexpr int kRedGroupWide = 4;
+// Cache-policy words of buffer loads and stores on gfx950: nt (streaming)
+// and sc1 (system scope).  Every byte here is touched once per pass.
+//  - The clip pass loads and stores nt (plain loads: 3.03 vs 2.80 ms at 8
+//    slices, 23.5 vs 22.6 ms at 64; plain stores 3.05 and 23.4 ms).
+//  - The step's full blocks store with sc1 and nt when the step streams (see
+//    kStepStreamBytes): 4.34 vs 4.41 ms with nt alone on an 872M-parameter
+//    shard, 4.90 with plain stores; the same write pattern without the
+//    arithmetic gains as much (4.39 vs 4.48 ms).  sc0 on top, or sc1 without
+//    nt, gains nothing.  Load policies (nt, sc0, sc1 in any combination) make
+//    no difference to either pass.
+constexpr int kCpolNt = 2;
+constexpr int kCpolSc1Nt = 16 | 2;
 // A step that moves at least this many bytes -- twice the 256 MB Infinity
 // Cache, so that none of its operands can stay cached from one step to the
-// next -- loads all its operands non-temporally (see k_step).
+// next -- loads all its operands non-temporally (see k_step).  A test build
+// lowers it to 0 to run the streaming step on small shards.
 #ifndef ZS_STEP_STREAM_BYTES
 #define ZS_STEP_STREAM_BYTES (int64_t(512) << 20)
 #endif
-#ifndef ZS_SQ_NT_LOAD
-#define ZS_SQ_NT_LOAD 1
-#endif
-#ifndef ZS_SQ_NT_STORE
-#define ZS_SQ_NT_STORE 1
-#endif
+constexpr int64_t kStepStreamBytes = ZS_STEP_STREAM_BYTES;
 // Block-to-data mapping.  Blocks are dispatched round robin over the 8 XCDs.
 // Plain: block b takes the b-th span, so neighbouring spans run on
 // different XCDs.  XCD-contiguous: the blocks of XCD x (b = x mod 8) take
@@ -124,34 +118,16 @@ __device__ __forceinline__ int64_t block_span(int64_t b, int64_t nb, bool xcd_co
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
-// Lane mapping of the clip pass's full blocks.  Plain: a lane reads the 8
-// consecutive elements of one vector (bf16: one 16-byte load per slice; fp32:
-// two 16-byte loads 16 bytes apart, so a wave's access covers 2 KB at a
-// 32-byte stride, as do the fp32 mean and accumulator accesses).
-// Contiguous: a lane takes 4 + 4 elements 256 apart, so every load or store
+// Lane mapping of the full blocks of the clip pass and the step: a lane takes
+// 4 + 4 elements 256 apart (the contiguous mapping), so every load or store
 // instruction of a wave covers one contiguous span (1 KB for fp32, 512 B for
-// bf16 read as 8-byte halves).  Measured on MI355X: contiguous is faster for
-// fp32 slices (6.07 -> 5.43 ms, 8 slices of 875M) and for 8 bf16 slices
-// (2.93 -> 2.83 ms; accumulation passes 13.3 -> 13.0 ms for 4), slower by
-// ~1% for 64 bf16 slices, which keep the plain mapping.
+// bf16 read as 8-byte halves), where a lane reading 8 consecutive elements
+// (the plain mapping) makes a wave's fp32 access cover 2 KB at a 32-byte
+// stride.  Measured on MI355X: contiguous is faster for fp32 slices (6.07 ->
+// 5.43 ms, 8 slices of 875M), for 8 bf16 slices (2.93 -> 2.83 ms;
+// accumulation passes 13.3 -> 13.0 ms for 4) and, with XCD-contiguous spans,
+// for 64 bf16 slices of 1.09B (22.35 vs 22.52 ms).
 
-// Gradient slices whose loads one thread has in flight at once; the wide
-// specializations (N_d >= ZS_SQ_WIDE_ND, one block per CU) keep fewer in
-// flight (64 slices of 1.09B: 24.04 vs 24.24 ms with 8, 24.75 with 3, 27.5
-// with 2; 8 slices: the same with 4 or 8).
-#ifndef ZS_RED_GROUP
-#define ZS_RED_GROUP 8
-#endif
-#ifndef ZS_RED_GROUP_WIDE
-#define ZS_RED_GROUP_WIDE 4
-#endif
-constexpr int kStepThreads = ZS_STEP_BS;
-constexpr int kStepU = ZS_STEP_U;
-constexpr bool kStepNtStore = ZS_STEP_NT_STORE != 0;
-constexpr int64_t kStepStreamBytes = ZS_STEP_STREAM_BYTES;
-constexpr bool kSqNtLoad = ZS_SQ_NT_LOAD != 0;
-constexpr bool kSqNtStore = ZS_SQ_NT_STORE != 0;
-constexpr int64_t kStepVecPerBlock = static_cast<int64_t>(ZS_STEP_BS) * ZS_STEP_U;
 constexpr int kFinalThreads = 1024;
 // Threads of one launch at most.  A dispatch counts its work-items in 32
 // bits, so a longer shard takes several launches, each with a grid below
@@ -185,34 +161,28 @@ __device__ __forceinline__ void store(T* p, T v)
     else *p = v;
 }
 
-// 16-byte store of four floats, non-temporal if NT.  (The step's stores
-// keep the hint; for the clip pass's stores the optimizer drops it, so that
-// pass uses buffer_store_f4 below.)
-template <bool NT>
-__device__ __forceinline__ void store_f4(f32x4* p, f32x4 v)
-{
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
-
 // A buffer resource over `bytes` bytes from `base` (uniform across the
-// wave), for 16-byte stores at per-lane byte offsets with an explicit cache
-// policy.  The generic non-temporal hint is lost by the optimizer on some
-// float-vector stores; the buffer store keeps it.
+// wave), for stores at per-lane byte offsets with an explicit cache-policy
+// word (the generic non-temporal hint is lost by the optimizer on some
+// float-vector stores, and it has no form for sc1).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, uint32_t bytes)
 {
     // dword 3: 32-bit data format, as CDNA raw buffer accesses require
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
 }
 
-constexpr int kCachePolicyNt = 2;   // the instruction's nt bit
-
-template <bool NT>
+template <int CPOL>
 __device__ __forceinline__ void buffer_store_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v)
 {
     const u32x4 b = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
                      __float_as_uint(v.w)};
-    __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, NT ? kCachePolicyNt : 0);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, CPOL);
+}
+
+template <int CPOL>
+__device__ __forceinline__ void buffer_store_u2(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CPOL);
 }
 
 // ---- bf16 --------------------------------------------------------------------
@@ -312,7 +282,7 @@ __device__ __forceinline__ void reduce_fetched(const Args& a, Fetch fetch, float
     }
     // Loads are issued G ranks at a time (bounded registers), the additions
     // stay in rank order.
-    constexpr int G = NDT >= ZS_SQ_WIDE_ND ? ZS_RED_GROUP_WIDE : ZS_RED_GROUP;
+    constexpr int G = NDT >= kSqWideNd ? kRedGroupWide : kRedGroup;
     for (int r0 = 1; r0 < nd; r0 += G) {
         typename IO::Raw b[G];
 #pragma unroll
@@ -446,8 +416,8 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
     f32x4 c0{}, c1{};
     if constexpr (ACC != kAccNone) {
         const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out);
-        c0 = load<kSqNtLoad>(p + i0);
-        c1 = load<kSqNtLoad>(p + i1);
+        c0 = load<true>(p + i0);
+        c1 = load<true>(p + i1);
     }
     float g[8];
     reduce_fetched<GT, NDT, WEIGHTED>(
@@ -455,11 +425,10 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
         [&](int r) {
             if constexpr (kF32) {
                 const f32x4* q4 = static_cast<const f32x4*>(a.slices.p[r]);
-                return typename SliceIO<float>::Raw{load<kSqNtLoad>(q4 + i0),
-                                                    load<kSqNtLoad>(q4 + i1)};
+                return typename SliceIO<float>::Raw{load<true>(q4 + i0), load<true>(q4 + i1)};
             } else {
                 const u32x2* q2 = static_cast<const u32x2*>(a.slices.p[r]);
-                const u32x2 lo = load<kSqNtLoad>(q2 + i0), hi = load<kSqNtLoad>(q2 + i1);
+                const u32x2 lo = load<true>(q2 + i0), hi = load<true>(q2 + i1);
                 return u32x4{lo.x, lo.y, hi.x, hi.y};
             }
         },
@@ -472,10 +441,10 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
     if constexpr (STORE) {
         const __amdgpu_buffer_rsrc_t mr =
             buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
-        buffer_store_f4<kSqNtStore>(mr, static_cast<uint32_t>((i0 - 2 * base) * 16),
-                                    f32x4{g[0], g[1], g[2], g[3]});
-        buffer_store_f4<kSqNtStore>(mr, static_cast<uint32_t>((i1 - 2 * base) * 16),
-                                    f32x4{g[4], g[5], g[6], g[7]});
+        buffer_store_f4<kCpolNt>(mr, static_cast<uint32_t>((i0 - 2 * base) * 16),
+                                 f32x4{g[0], g[1], g[2], g[3]});
+        buffer_store_f4<kCpolNt>(mr, static_cast<uint32_t>((i1 - 2 * base) * 16),
+                                 f32x4{g[4], g[5], g[6], g[7]});
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -484,113 +453,58 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
     }
 }
 
-// A full block in the plain lane mapping (U vectors per thread).
-template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
-__device__ __forceinline__ void reduce_block_plain(const SqArgs& a, int64_t base, double& q)
-{
-    constexpr int BS = kSqThreads, U = ZS_SQ_U;
-    f32x4 acc0[U], acc1[U];
-    if constexpr (ACC != kAccNone) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out) + 2 * (base + u * BS + threadIdx.x);
-            acc0[u] = load<kSqNtLoad>(p);
-            acc1[u] = load<kSqNtLoad>(p + 1);
-        }
-    }
-    float g[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        reduce_vec<GT, NDT, WEIGHTED, kSqNtLoad>(a, base + u * BS + threadIdx.x, g[u]);
-    if constexpr (ACC != kAccNone) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float ac[8] = {acc0[u].x, acc0[u].y, acc0[u].z, acc0[u].w,
-                                 acc1[u].x, acc1[u].y, acc1[u].z, acc1[u].w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) g[u][j] = accumulate1<ACC>(a, ac[j], g[u][j]);
-        }
-    }
-    // The block's kSqVecPerBlock * 32 bytes of the output (unused when
-    // it is not stored: then mean_out is null and nothing is written
-    // through it).
-    const __amdgpu_buffer_rsrc_t mr =
-        buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if constexpr (STORE) {
-            const uint32_t off = static_cast<uint32_t>((u * BS + threadIdx.x) * 32);
-            buffer_store_f4<kSqNtStore>(mr, off, f32x4{g[u][0], g[u][1], g[u][2], g[u][3]});
-            buffer_store_f4<kSqNtStore>(mr, off + 16, f32x4{g[u][4], g[u][5], g[u][6], g[u][7]});
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const double d = g[u][j];
-            q = sq_add(q, d);
-        }
-    }
-}
-
 // Clip pass 1: the reduced gradient of the slices (optionally stored, or
 // accumulated over micro-batches) and one fp64 partial sum of its squares
 // per block.  Block span s (see block_span) owns kSqVecPerBlock consecutive
-// vectors.  Contiguous mapping: lane l of the block's wave w takes elements
-// 4l..4l+3 and 256+4l..256+4l+3 of the wave's 512.  Plain mapping: thread x
-// reduces vectors base + u*BS + x, u = 0..U-1, issuing all their loads
-// first.  Either way a thread adds its squares in a fixed order, and only
-// the last block of a shard, which meets the partial vector or runs past
-// valid_len, takes the guarded element-wise path.
+// vectors; lane l of the block's wave w takes elements 4l..4l+3 and
+// 256+4l..256+4l+3 of the wave's 512 (the contiguous lane mapping).  A thread
+// adds its squares in a fixed order, and only the last block of a shard,
+// which meets the partial vector or runs past valid_len, takes the guarded
+// path (vector by vector, then element by element).
 template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
 __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
 {
     static_assert(STORE || ACC == kAccNone, "an accumulator is always stored");
-    constexpr int BS = kSqThreads, U = ZS_SQ_U;
+    static_assert(kSqThreads % 64 == 0, "whole waves");
     const int64_t nfull = a.valid_len >> 3;
     const int64_t span = block_span(blockIdx.x, gridDim.x, a.xcd_contiguous != 0);
     const int64_t base = a.v0 + span * kSqVecPerBlock;
     double q = 0.0;
     if (base + kSqVecPerBlock <= nfull) {
-        if constexpr (U == 1 && BS % 64 == 0) {
-            if (a.contiguous) reduce_block_contiguous<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
-            else reduce_block_plain<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
-        } else {
-            reduce_block_plain<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
-        }
+        reduce_block_contiguous<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
     } else {
-        for (int u = 0; u < U; ++u) {
-            const int64_t vi = base + u * BS + threadIdx.x;
-            if (vi < nfull) {
-                float g[8];
-                reduce_vec<GT, NDT, WEIGHTED, kSqNtLoad>(a, vi, g);
-                f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
-                if constexpr (ACC != kAccNone) {
-                    const f32x4 c0 = o[0], c1 = o[1];
-                    const float ac[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const int64_t vi = base + threadIdx.x;
+        if (vi < nfull) {
+            float g[8];
+            reduce_vec<GT, NDT, WEIGHTED, true>(a, vi, g);
+            f32x4* o = reinterpret_cast<f32x4*>(a.mean_out) + 2 * vi;
+            if constexpr (ACC != kAccNone) {
+                const f32x4 c0 = o[0], c1 = o[1];
+                const float ac[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) g[j] = accumulate1<ACC>(a, ac[j], g[j]);
-                }
-                if constexpr (STORE) {
-                    store_f4<kSqNtStore>(o, f32x4{g[0], g[1], g[2], g[3]});
-                    store_f4<kSqNtStore>(o + 1, f32x4{g[4], g[5], g[6], g[7]});
-                }
+                for (int j = 0; j < 8; ++j) g[j] = accumulate1<ACC>(a, ac[j], g[j]);
+            }
+            if constexpr (STORE) {
+                store<true>(o, f32x4{g[0], g[1], g[2], g[3]});
+                store<true>(o + 1, f32x4{g[4], g[5], g[6], g[7]});
+            }
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const double d = g[j];
-                    q = sq_add(q, d);
-                }
-            } else if (vi == nfull) {
-                for (int64_t i = vi * 8; i < a.valid_len; ++i) {
-                    float g = reduce_one<GT, NDT, WEIGHTED>(a, i);
-                    if constexpr (ACC != kAccNone) g = accumulate1<ACC>(a, a.mean_out[i], g);
-                    if constexpr (STORE) a.mean_out[i] = g;
-                    const double d = g;
-                    q = sq_add(q, d);
-                }
+            for (int j = 0; j < 8; ++j) {
+                const double d = g[j];
+                q = sq_add(q, d);
+            }
+        } else if (vi == nfull) {
+            for (int64_t i = vi * 8; i < a.valid_len; ++i) {
+                float g = reduce_one<GT, NDT, WEIGHTED>(a, i);
+                if constexpr (ACC != kAccNone) g = accumulate1<ACC>(a, a.mean_out[i], g);
+                if constexpr (STORE) a.mean_out[i] = g;
+                const double d = g;
+                q = sq_add(q, d);
             }
         }
     }
     if (a.partials) {   // uniform: every thread of the block takes the same branch
-        const double t = block_sum<BS>(q);
+        const double t = block_sum<kSqThreads>(q);
         if (threadIdx.x == 0) a.partials[span] = t;
     }
 }
@@ -647,11 +561,8 @@ __device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c,
     a.out[i] = static_cast<uint16_t>(bf16_rne(w));
 }
 
-// AdamW on U vectors held in registers, bias corrections resolved, each
-// vector stored as soon as it is computed: while vector u is computed, the
-// loads of vectors u+1.. are still in flight (software pipelining across the
-// thread's vectors).
-// AdamW on a lane's 8 parameters (clipped gradient when CLIP).
+// AdamW on a lane's 8 parameters (clipped gradient when CLIP), bias
+// corrections resolved.
 template <bool CLIP, bool BC1_POW2, bool BC2_POW2>
 __device__ __forceinline__ void adamw8(const StepConsts& c, float coef, const float (&g)[8],
                                        float (&W)[8], float (&M)[8], float (&V)[8])
@@ -664,15 +575,42 @@ __device__ __forceinline__ void adamw8(const StepConsts& c, float coef, const fl
     }
 }
 
+// The arithmetic of one lane's 8 parameters after its loads: the clip
+// coefficient, then AdamW under a uniform branch on this step's bias
+// corrections.  The scheduling barriers keep every load ahead of any
+// arithmetic, so a wave waits for memory once and computes the fp64 clip
+// coefficient while its loads are in flight.
+template <bool CLIP>
+__device__ __forceinline__ void step_arith(const StepArgs& a, const float (&g)[8], float (&W)[8],
+                                           float (&M)[8], float (&V)[8])
+{
+    __builtin_amdgcn_sched_barrier(0);
+    float coef = 1.0f;
+    if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
+    __builtin_amdgcn_sched_barrier(0);
+    const StepConsts c = a.c;
+    if (c.bc1_pow2) {
+        if (c.bc2_pow2) adamw8<CLIP, true, true>(c, coef, g, W, M, V);
+        else adamw8<CLIP, true, false>(c, coef, g, W, M, V);
+    } else {
+        if (c.bc2_pow2) adamw8<CLIP, false, true>(c, coef, g, W, M, V);
+        else adamw8<CLIP, false, false>(c, coef, g, W, M, V);
+    }
+}
+
 // A full block of the step in the contiguous lane mapping: lane l of wave w
 // owns the parameters 4l..4l+3 and 256+4l..256+4l+3 of the wave's 512, i.e.
 // the f32x4 groups q0 and q1 = q0 + 64 of the fp32 arrays (and the 8-byte
 // groups q0, q1 of the bf16 ones), so every load and store instruction of a
-// wave covers one contiguous span.
-template <int BS, bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
+// wave covers one contiguous span.  Stores go through buffer resources over
+// the block's tile of each array with the cache-policy word CPOL.
+template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t base)
 {
-    const int64_t q0 = 2 * base + (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
+    static_assert(kStepThreads % 64 == 0, "whole waves");
+    constexpr int CPOL = STREAM ? kCpolSc1Nt : kCpolNt;
+    const int64_t r0 = (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);   // in the block's tile
+    const int64_t q0 = 2 * base + r0;
     const int64_t q1 = q0 + 64;
     const f32x4* w4 = reinterpret_cast<const f32x4*>(a.w);
     const f32x4* m4 = reinterpret_cast<const f32x4*>(a.m);
@@ -696,112 +634,61 @@ __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t
     const f32x4 w0 = load<STREAM>(w4 + q0), w1 = load<STREAM>(w4 + q1);
     const f32x4 m0 = load<STREAM>(m4 + q0), m1 = load<STREAM>(m4 + q1);
     const f32x4 v0 = load<STREAM>(v4 + q0), v1 = load<STREAM>(v4 + q1);
-    __builtin_amdgcn_sched_barrier(0);
-    float coef = 1.0f;
-    if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
-    __builtin_amdgcn_sched_barrier(0);
-    const StepConsts c = a.c;
     float W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
     float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    if (c.bc1_pow2) {
-        if (c.bc2_pow2) adamw8<CLIP, true, true>(c, coef, g, W, M, V);
-        else adamw8<CLIP, true, false>(c, coef, g, W, M, V);
-    } else {
-        if (c.bc2_pow2) adamw8<CLIP, false, true>(c, coef, g, W, M, V);
-        else adamw8<CLIP, false, false>(c, coef, g, W, M, V);
-    }
-    constexpr bool NT = kStepNtStore;
-    f32x4* wo = reinterpret_cast<f32x4*>(a.w);
-    f32x4* mo = reinterpret_cast<f32x4*>(a.m);
-    f32x4* vo = reinterpret_cast<f32x4*>(a.v);
-    u32x2* oo = reinterpret_cast<u32x2*>(a.out);
-    store_f4<NT>(wo + q0, f32x4{W[0], W[1], W[2], W[3]});
-    store_f4<NT>(wo + q1, f32x4{W[4], W[5], W[6], W[7]});
-    store_f4<NT>(mo + q0, f32x4{M[0], M[1], M[2], M[3]});
-    store_f4<NT>(mo + q1, f32x4{M[4], M[5], M[6], M[7]});
-    store_f4<NT>(vo + q0, f32x4{V[0], V[1], V[2], V[3]});
-    store_f4<NT>(vo + q1, f32x4{V[4], V[5], V[6], V[7]});
-    store<NT>(oo + q0, u32x2{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3])});
-    store<NT>(oo + q1, u32x2{pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
+    step_arith<CLIP>(a, g, W, M, V);
+    // the block's tile: kStepVecPerBlock * 32 bytes of each fp32 array, half
+    // that of the bf16 slot; the lane's byte offsets in it
+    constexpr uint32_t kTile = static_cast<uint32_t>(kStepVecPerBlock * 32);
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + base * 8, kTile);
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(a.m + base * 8, kTile);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + base * 8, kTile);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(a.out + base * 8, kTile / 2);
+    const uint32_t b0 = static_cast<uint32_t>(r0 * 16), b1 = b0 + 64 * 16;
+    buffer_store_f4<CPOL>(rw, b0, f32x4{W[0], W[1], W[2], W[3]});
+    buffer_store_f4<CPOL>(rw, b1, f32x4{W[4], W[5], W[6], W[7]});
+    buffer_store_f4<CPOL>(rm, b0, f32x4{M[0], M[1], M[2], M[3]});
+    buffer_store_f4<CPOL>(rm, b1, f32x4{M[4], M[5], M[6], M[7]});
+    buffer_store_f4<CPOL>(rv, b0, f32x4{V[0], V[1], V[2], V[3]});
+    buffer_store_f4<CPOL>(rv, b1, f32x4{V[4], V[5], V[6], V[7]});
+    buffer_store_u2<CPOL>(ro, b0 / 2, u32x2{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3])});
+    buffer_store_u2<CPOL>(ro, b1 / 2, u32x2{pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
 }
 
-template <int U, int BS, bool CLIP, bool BC1_POW2, bool BC2_POW2>
-__device__ __forceinline__ void adamw_store_vectors(const StepArgs& a, const StepConsts& c,
-                                                    float coef, int64_t vi,
-                                                    const float (&g)[U][8], const f32x4 (&w0)[U],
-                                                    const f32x4 (&w1)[U], const f32x4 (&m0)[U],
-                                                    const f32x4 (&m1)[U], const f32x4 (&v0)[U],
-                                                    const f32x4 (&v1)[U])
+// One full vector vi of the step in the plain mapping (8 consecutive
+// parameters; the block that meets valid_len).
+template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
+__device__ __forceinline__ void step_vector(const StepArgs& a, int64_t vi)
 {
-    f32x4* w4 = reinterpret_cast<f32x4*>(a.w);
-    f32x4* m4 = reinterpret_cast<f32x4*>(a.m);
-    f32x4* v4 = reinterpret_cast<f32x4*>(a.v);
-    u32x4* o4 = reinterpret_cast<u32x4*>(a.out);
-    constexpr bool NT = kStepNtStore;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float W[8] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w, w1[u].x, w1[u].y, w1[u].z, w1[u].w};
-        float M[8] = {m0[u].x, m0[u].y, m0[u].z, m0[u].w, m1[u].x, m1[u].y, m1[u].z, m1[u].w};
-        float V[8] = {v0[u].x, v0[u].y, v0[u].z, v0[u].w, v1[u].x, v1[u].y, v1[u].z, v1[u].w};
-        adamw8<CLIP, BC1_POW2, BC2_POW2>(c, coef, g[u], W, M, V);
-        const int64_t x = vi + u * BS;
-        store_f4<NT>(w4 + 2 * x, f32x4{W[0], W[1], W[2], W[3]});
-        store_f4<NT>(w4 + 2 * x + 1, f32x4{W[4], W[5], W[6], W[7]});
-        store_f4<NT>(m4 + 2 * x, f32x4{M[0], M[1], M[2], M[3]});
-        store_f4<NT>(m4 + 2 * x + 1, f32x4{M[4], M[5], M[6], M[7]});
-        store_f4<NT>(v4 + 2 * x, f32x4{V[0], V[1], V[2], V[3]});
-        store_f4<NT>(v4 + 2 * x + 1, f32x4{V[4], V[5], V[6], V[7]});
-        store<NT>(o4 + x, u32x4{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3]),
-                                pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
-    }
-}
-
-// U full vectors at vi, vi + BS, ...: all loads, then the clip coefficient,
-// then vector by vector the arithmetic and the stores.  The scheduling
-// barrier keeps every load ahead of any arithmetic, so a wave waits for
-// memory once and computes the fp64 clip coefficient while its loads are in
-// flight.  A uniform branch picks the arithmetic for this step's bias
-// corrections.
-template <int U, int BS, bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
-__device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
-{
-    const f32x4* w4 = reinterpret_cast<const f32x4*>(a.w);
-    const f32x4* m4 = reinterpret_cast<const f32x4*>(a.m);
-    const f32x4* v4 = reinterpret_cast<const f32x4*>(a.v);
-    float g[U][8];
-    f32x4 w0[U], w1[U], m0[U], m1[U], v0[U], v1[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t x = vi + u * BS;
-        if constexpr (FROM_SLICES) {
-            reduce_vec<uint16_t, NDT, false, STREAM>(a, x, g[u]);
-        } else {
-            const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * x;
-            const f32x4 x0 = load<STREAM>(g4), x1 = load<STREAM>(g4 + 1);
-            g[u][0] = x0.x; g[u][1] = x0.y; g[u][2] = x0.z; g[u][3] = x0.w;
-            g[u][4] = x1.x; g[u][5] = x1.y; g[u][6] = x1.z; g[u][7] = x1.w;
-        }
-        w0[u] = load<STREAM>(w4 + 2 * x); w1[u] = load<STREAM>(w4 + 2 * x + 1);
-        m0[u] = load<STREAM>(m4 + 2 * x); m1[u] = load<STREAM>(m4 + 2 * x + 1);
-        v0[u] = load<STREAM>(v4 + 2 * x); v1[u] = load<STREAM>(v4 + 2 * x + 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float coef = 1.0f;
-    if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
-    __builtin_amdgcn_sched_barrier(0);
-    const StepConsts c = a.c;
-    if (c.bc1_pow2) {
-        if (c.bc2_pow2)
-            adamw_store_vectors<U, BS, CLIP, true, true>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
-        else
-            adamw_store_vectors<U, BS, CLIP, true, false>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
+    f32x4* w4 = reinterpret_cast<f32x4*>(a.w) + 2 * vi;
+    f32x4* m4 = reinterpret_cast<f32x4*>(a.m) + 2 * vi;
+    f32x4* v4 = reinterpret_cast<f32x4*>(a.v) + 2 * vi;
+    float g[8];
+    if constexpr (FROM_SLICES) {
+        reduce_vec<uint16_t, NDT, false, STREAM>(a, vi, g);
     } else {
-        if (c.bc2_pow2)
-            adamw_store_vectors<U, BS, CLIP, false, true>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
-        else
-            adamw_store_vectors<U, BS, CLIP, false, false>(a, c, coef, vi, g, w0, w1, m0, m1, v0, v1);
+        const f32x4* g4 = reinterpret_cast<const f32x4*>(a.mean) + 2 * vi;
+        const f32x4 x0 = load<STREAM>(g4), x1 = load<STREAM>(g4 + 1);
+        g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w;
+        g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
     }
+    const f32x4 w0 = load<STREAM>(w4), w1 = load<STREAM>(w4 + 1);
+    const f32x4 m0 = load<STREAM>(m4), m1 = load<STREAM>(m4 + 1);
+    const f32x4 v0 = load<STREAM>(v4), v1 = load<STREAM>(v4 + 1);
+    float W[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    step_arith<CLIP>(a, g, W, M, V);
+    store<true>(w4, f32x4{W[0], W[1], W[2], W[3]});
+    store<true>(w4 + 1, f32x4{W[4], W[5], W[6], W[7]});
+    store<true>(m4, f32x4{M[0], M[1], M[2], M[3]});
+    store<true>(m4 + 1, f32x4{M[4], M[5], M[6], M[7]});
+    store<true>(v4, f32x4{V[0], V[1], V[2], V[3]});
+    store<true>(v4 + 1, f32x4{V[4], V[5], V[6], V[7]});
+    store<true>(reinterpret_cast<u32x4*>(a.out) + vi,
+                u32x4{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3]),
+                      pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
 }
 
 // The fused step over the slot's shard_len/8 vectors: gradient (mean of the
@@ -812,45 +699,39 @@ __device__ __forceinline__ void step_vectors(const StepArgs& a, int64_t vi)
 // measured against the plain one on MI355X (interleaved medians, one box),
 // 4.40 vs 4.47 ms for 875M parameters, 5.33 vs 5.51 ms for 1.09B, 70 vs 75 us
 // for 15.6M.  The block that meets valid_len takes the plain path per vector.
-// STREAM: every operand is loaded non-temporally.  Measured with the
-// contiguous mapping (interleaved medians, one box): the stored gradient and
-// v non-temporal, 4.40 vs 4.62 ms for 875M parameters, 5.65 vs 5.82 ms for
-// 1.09B, 4.40 vs 4.55 ms for 32 calls of 27M; w and m as well, 4.32 vs 4.41,
-// 5.57 vs 5.65 and 4.18 vs 4.41 ms.  A 15.6M-parameter step, whose 467 MB of
-// operands back-to-back steps find partly in the 256 MB Infinity Cache,
-// loses (74 vs 70 us), so the host picks STREAM from the bytes the step
-// moves (ZS_STEP_STREAM_BYTES).
+// STREAM: every operand is loaded non-temporally and the full blocks store
+// with sc1 as well as nt.  Measured with the contiguous mapping (interleaved
+// medians, one box): the stored gradient and v non-temporal, 4.40 vs 4.62 ms
+// for 875M parameters, 5.65 vs 5.82 ms for 1.09B, 4.40 vs 4.55 ms for 32
+// calls of 27M; w and m as well, 4.32 vs 4.41, 5.57 vs 5.65 and 4.18 vs
+// 4.41 ms.  A 15.6M-parameter step, whose 467 MB of operands back-to-back
+// steps find partly in the 256 MB Infinity Cache, loses (74 vs 70 us), so
+// the host picks STREAM from the bytes the step moves (kStepStreamBytes).
 template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 __global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
 {
-    constexpr int BS = kStepThreads, U = kStepU;
     const int64_t nfull = a.valid_len >> 3;
     const int64_t nslot = a.shard_len >> 3;
     const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kStepVecPerBlock;
     if (base + kStepVecPerBlock <= nfull) {
-        if constexpr (ZS_STEP_CONTIG && U == 1 && BS % 64 == 0)
-            step_block_contiguous<BS, FROM_SLICES, NDT, CLIP, STREAM>(a, base);
-        else
-            step_vectors<U, BS, FROM_SLICES, NDT, CLIP, STREAM>(a, base + threadIdx.x);
+        step_block_contiguous<FROM_SLICES, NDT, CLIP, STREAM>(a, base);
         return;
     }
-    for (int u = 0; u < U; ++u) {
-        const int64_t vi = base + u * BS + threadIdx.x;
-        if (vi < nfull) {
-            step_vectors<1, BS, FROM_SLICES, NDT, CLIP, STREAM>(a, vi);
-        } else if (vi < nslot) {
-            // The partial vector (its valid elements), then pads.
-            int64_t i = vi * 8;
-            if (i < a.valid_len) {
-                float coef = 1.0f;
-                if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
-                for (; i < a.valid_len; ++i) step_one<FROM_SLICES, NDT, CLIP>(a, a.c, coef, i);
-            }
-            if (i == vi * 8) {
-                reinterpret_cast<u32x4*>(a.out)[vi] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                for (; i < vi * 8 + 8; ++i) a.out[i] = 0;
-            }
+    const int64_t vi = base + threadIdx.x;
+    if (vi < nfull) {
+        step_vector<FROM_SLICES, NDT, CLIP, STREAM>(a, vi);
+    } else if (vi < nslot) {
+        // The partial vector (its valid elements), then pads.
+        int64_t i = vi * 8;
+        if (i < a.valid_len) {
+            float coef = 1.0f;
+            if constexpr (CLIP) coef = clip_coef(*a.sqnorm + a.other_sqnorm, a.max_norm);
+            for (; i < a.valid_len; ++i) step_one<FROM_SLICES, NDT, CLIP>(a, a.c, coef, i);
+        }
+        if (i == vi * 8) {
+            reinterpret_cast<u32x4*>(a.out)[vi] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            for (; i < vi * 8 + 8; ++i) a.out[i] = 0;
         }
     }
 }
@@ -940,9 +821,8 @@ int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
     // fp32 slices (16 loads per thread at N_d = 8), accumulation passes
     // (the accumulator's loads on top) and wide bf16 reductions keep enough
     // bytes in flight at one block per CU
-    const bool wide = std::is_same<GT, float>::value || ACC != kAccNone ||
-                      a.n_d >= ZS_SQ_WIDE_ND;
-    const int per_cu = wide ? ZS_SQ_WIDE_PER_CU : ZS_SQ_PER_CU;
+    const bool wide = std::is_same<GT, float>::value || ACC != kAccNone || a.n_d >= kSqWideNd;
+    const int per_cu = wide ? kSqWidePerCu : kSqPerCu;
     const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>>(per_cu, &lds);
     if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
     hipLaunchKernelGGL((k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>), dim3(blocks),
@@ -1027,7 +907,7 @@ template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 int launch_step_k(const StepArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
-    const int rc = lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(ZS_STEP_PER_CU, &lds);
+    const int rc = lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(kStepPerCu, &lds);
     if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
     hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, CLIP, STREAM>), dim3(blocks),
                        dim3(kStepThreads), lds, st, a);
@@ -1119,9 +999,8 @@ int prepare_device()
 int enqueue_reduce(SqArgs a, bool f32, bool weighted, int acc, bool store, double* partials,
                    void* stream)
 {
-    // block-to-data and lane mappings (see block_span and k_reduce_sqnorm)
-    a.xcd_contiguous = a.n_d >= ZS_SQ_WIDE_ND ? 1 : 0;
-    a.contiguous = (f32 || a.n_d < ZS_SQ_WIDE_ND) ? 1 : 0;
+    // block-to-data mapping (see block_span)
+    a.xcd_contiguous = a.n_d >= kSqWideNd ? 1 : 0;
     const bool general = f32 || weighted || acc != kAccNone;
     const int64_t blocks = sq_blocks(a.valid_len);
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -194,6 +194,30 @@ def test_ragged_shapes(mode):
     log(f"ragged shapes, mode {mode}: {n_cases} cases")
 
 
+@pytest.mark.parametrize("n_d", [16, 32])
+def test_specialized_nd_16_and_32(n_d):
+    """The kernels specialized for 16 and 32 slices (the fused step from the
+    slices, the clip pass with and without the stored mean), on ragged
+    shards of the first and the last rank, against the oracle."""
+    rng = np.random.default_rng(1000 + n_d)
+    for psi in (n_d * 6000 + 7, n_d * 70_001):
+        for rank in (0, n_d - 1):
+            s = Z.zs_layout(psi, n_d, rank, 8, 2)
+            V = s.valid_len
+            sl = [O.bf16_rne(rng.normal(0, 1e-3, V).astype(np.float32)) for _ in range(n_d)]
+            w = rng.normal(0, 0.02, V).astype(np.float32)
+            m = rng.normal(0, 1e-4, V).astype(np.float32)
+            v = np.abs(rng.normal(0, 1e-6, V)).astype(np.float32)
+            for mode in ("slices", "mean", "reread"):
+                h = O.Hparams(lr=3e-4, weight_decay=0.1, step=9,
+                              max_grad_norm=0.0 if mode == "slices" else 0.05)
+                res = run_small_case(psi, n_d, rank, 8, 2, Z.ZS_OUT_GATHER, zs_h(h), sl, w, m,
+                                     v, mode)
+                check_against_oracle((psi, n_d, rank, mode), res[0], res, sl, w, m, v, h, 0.0,
+                                     mode)
+    log(f"N_d = {n_d}: fused step, clip pass (stored and not) bit-exact")
+
+
 def test_stage0_ddp_equals_concatenated_shards():
     """One DDP step (stage 0: every rank updates the whole vector) equals the
     concatenation of the N_d ZeRO shard steps, bit for bit, on the GPU."""
