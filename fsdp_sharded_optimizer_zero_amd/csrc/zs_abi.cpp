@@ -73,8 +73,8 @@ int sqnorm_pass(const zs_shard* s, const uint16_t* const* grad_slices, float* me
     if (rc != ZS_OK) return rc;
     rc = enqueue_reduce(a, false, false, kAccNone, mean_out != nullptr, partials, stream);
     if (rc != ZS_OK) return rc;
-    return enqueue_sqnorm_sums(partials, sq_blocks(s->valid_len), 1, sqnorm_out, accumulate,
-                               stream);
+    return enqueue_sqnorm_sums(partials, reduce_blocks(s->valid_len, s->n_d, false, kAccNone), 1,
+                               sqnorm_out, accumulate, stream);
 }
 
 }  // namespace
@@ -134,7 +134,7 @@ extern "C" int shard_grad_sqnorm_units(const zs_shard* s, int32_t units,
         if (rc != ZS_OK) return rc;
         if (mean_out && mean_out[u] && !aligned16(mean_out[u])) return ZS_EALIGN;
     }
-    const int64_t blocks = sq_blocks(s->valid_len);
+    const int64_t blocks = reduce_blocks(s->valid_len, s->n_d, false, kAccNone);
     double* partials = static_cast<double*>(workspace);
     for (int32_t u = 0; u < units; ++u) {
         SqArgs a = reduce_args(s, mean_out ? mean_out[u] : nullptr, 1);
@@ -182,10 +182,11 @@ extern "C" int shard_grad_reduce(const zs_shard* s, const zs_reduce* r,
     const int acc = r->micro == 0 ? kAccNone
                   : (r->micro == r->micro_count - 1 ? kAccFinal : kAccAdd);
     double* partials = sqnorm_out ? static_cast<double*>(workspace) : nullptr;
-    rc = enqueue_reduce(a, r->grad_dtype == ZS_GRAD_F32, weighted, acc, true, partials, stream);
+    const bool f32 = r->grad_dtype == ZS_GRAD_F32;
+    rc = enqueue_reduce(a, f32, weighted, acc, true, partials, stream);
     if (rc != ZS_OK || !sqnorm_out) return rc;
-    return enqueue_sqnorm_sums(partials, sq_blocks(s->valid_len), 1, sqnorm_out, accumulate,
-                               stream);
+    return enqueue_sqnorm_sums(partials, reduce_blocks(s->valid_len, s->n_d, f32, acc), 1,
+                               sqnorm_out, accumulate, stream);
 }
 
 extern "C" int zero_shard_step(const zs_shard* s, const zs_adamw* h,

@@ -20,18 +20,18 @@ struct StepConsts {
     int32_t bc1_pow2, bc2_pow2;
 };
 
-// Launch shape of the clip pass: threads per block, one 8-parameter vector
-// per thread.  The pass writes one fp64 partial sum per block into the
-// workspace.
-constexpr int kSqThreads = 512;
-constexpr int64_t kSqVecPerBlock = kSqThreads;
+// The clip pass runs blocks of 256 or 512 threads (one 8-parameter vector
+// per thread, the size chosen per call by the kernel part) and writes one
+// fp64 partial sum per block into the workspace; the workspace is sized for
+// the smaller block.
+constexpr int kSqThreadsMin = 256;
 
-// Blocks of the clip pass over valid_len parameters: one per kSqVecPerBlock
-// vectors of 8 (the last vector may be partial).
-inline int64_t sq_blocks(int64_t valid_len)
+// Blocks of the clip pass over valid_len parameters at `threads` threads per
+// block (the last vector may be partial).
+inline int64_t sq_blocks(int64_t valid_len, int threads = kSqThreadsMin)
 {
     const int64_t nvec = (valid_len + 7) / 8;
-    return (nvec + kSqVecPerBlock - 1) / kSqVecPerBlock;
+    return (nvec + threads - 1) / threads;
 }
 
 // The block partials are summed in two fixed-order stages: groups of
@@ -75,7 +75,6 @@ struct SqArgs {
     float inv_nd;
     float micro_count;      // m, the divisor of the last micro-batch
     float inv_micro_count;  // 1/m when m is a power of two (exact), else 0
-    int32_t xcd_contiguous; // block-to-data mapping (set by enqueue_reduce)
 };
 
 // What the clip pass does with the accumulator: write the reduced slice
@@ -86,8 +85,11 @@ enum AccMode { kAccNone = 0, kAccAdd = 1, kAccFinal = 2 };
 // The passes (zs_kernels.hip).  Each enqueues its launches on `stream` (a
 // hipStream_t), splitting a grid longer than one launch may hold, and
 // returns ZS_OK or ZS_ELAUNCH; arguments are validated by the caller.
+//   reduce_blocks: the number of blocks (fp64 partials) the clip pass runs
+//     over valid_len parameters for this reduction (at most
+//     sq_blocks(valid_len)).
 //   enqueue_reduce: the clip pass / general reduction over a.valid_len
-//     (a.v0 and a.partials are set per launch; partials: sq_blocks(valid_len)
+//     (a.v0 and a.partials are set per launch; partials: reduce_blocks(...)
 //     fp64 slots, or null for no norm).  f32/weighted/acc select the general
 //     reduction (always stored); otherwise bf16 rank-order mean, stored iff
 //     `store`.
@@ -95,6 +97,7 @@ enum AccMode { kAccNone = 0, kAccAdd = 1, kAccFinal = 2 };
 //     (added to it if accumulate), in a fixed order.
 //   enqueue_step: the fused AdamW step over a.shard_len (a.v0 set per launch).
 //   enqueue_pack: bf16 cast of master[0, valid_len) and +0 pads into out.
+int64_t reduce_blocks(int64_t valid_len, int32_t n_d, bool f32, int acc);
 int enqueue_reduce(SqArgs a, bool f32, bool weighted, int acc, bool store, double* partials,
                    void* stream);
 int enqueue_sqnorm_sums(double* partials, int64_t blocks, int32_t units, double* sqnorm_out,

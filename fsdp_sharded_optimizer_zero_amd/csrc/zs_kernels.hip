@@ -66,16 +66,25 @@ constexpr int64_t kStepVecPerBlock = kStepThreads;
 // 872M-parameter shard at two 256-thread blocks per CU, 5.10 at one (its
 // division and square-root chain exposed), 4.60 at three, 4.84 uncapped;
 // 512-thread blocks at one per CU, or 2 or 4 vectors per thread, 4.62-4.83.
-// The clip pass is fastest at two 512-thread blocks per CU over 8 bf16 slices,
-// and at one for 64 slices, for fp32 slices and for the accumulation passes
-// (more loads per thread).
+// The clip pass's shape is sq_shape below.
 constexpr int kStepPerCu = 2;
-constexpr int kSqPerCu = 2;
-// The clip pass with this many slices or more keeps enough loads in flight
-// per thread to run at one block per CU; fp32 slices and accumulation passes
-// run there too.
+// Launch shape of the clip pass.  A bf16 reduction of kSqWideNd slices or
+// more keeps enough loads in flight per thread to run 512-thread blocks at
+// one per CU (64 slices of 1.09B: 22.4 ms, against 22.5 ms at two 256-thread
+// blocks); every other reduction runs 256-thread blocks at two per CU (8
+// bf16 slices of 875M: 2.61 ms, against 2.82 ms at two 512-thread blocks).
+// The workspace is sized for 256-thread blocks (kSqThreadsMin).
 constexpr int kSqWideNd = 32;
-constexpr int kSqWidePerCu = 1;
+// The wide shape also maps blocks XCD-contiguously (see block_span).
+constexpr int kSqWideThreads = 512;
+struct SqShape {
+    int threads, per_cu;
+};
+constexpr SqShape sq_shape(int32_t n_d, bool f32, int acc)
+{
+    return (!f32 && acc == kAccNone && n_d >= kSqWideNd) ? SqShape{kSqWideThreads, 1}
+                                                          : SqShape{kSqThreadsMin, 2};
+}
 // Gradient slices whose loads one thread has in flight at once; the wide
 // specializations (N_d >= kSqWideNd, one block per CU) keep fewer in flight
 // (64 slices of 1.09B: 24.04 vs 24.24 ms with 8, 24.75 with 3, 27.5 with 2;
@@ -106,8 +115,10 @@ constexpr int64_t kStepStreamBytes = ZS_STEP_STREAM_BYTES;
 // Plain: block b takes the b-th span, so neighbouring spans run on
 // different XCDs.  XCD-contiguous: the blocks of XCD x (b = x mod 8) take
 // one contiguous eighth of the spans.  Measured on MI355X: the clip pass
-// over 64 slices is ~3% faster XCD-contiguous (23.0 vs 23.7 ms), over 8
-// slices ~3.5% slower; the step is within 1% either way, and stays plain.
+// over 64 slices is ~3% faster XCD-contiguous (23.0 vs 23.7 ms; 22.4 vs
+// 23.1 ms with the contiguous lane mapping), over 8 slices ~3.5% slower; the
+// step is within 1% either way, and stays plain.  The clip pass takes it
+// with its wide shape (sq_shape).
 constexpr int kXcds = 8;
 
 // Logical span of dispatched block b of nb (a bijection on [0, nb)).
@@ -183,6 +194,20 @@ template <int CPOL>
 __device__ __forceinline__ void buffer_store_u2(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v)
 {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, CPOL);
+}
+
+template <int CPOL>
+__device__ __forceinline__ f32x4 buffer_load_f4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL);
+    return f32x4{__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z),
+                 __uint_as_float(b.w)};
+}
+
+template <int CPOL>
+__device__ __forceinline__ u32x2 buffer_load_u2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CPOL);
 }
 
 // ---- bf16 --------------------------------------------------------------------
@@ -380,15 +405,60 @@ __device__ __forceinline__ float clip_coef(double Q, double max_norm)
 // multiply followed by the add.
 __device__ __forceinline__ double sq_add(double q, double d) { return __builtin_fma(d, d, q); }
 
-// ---- deterministic fp64 block sum (result valid in thread 0) ------------------
+// ---- deterministic fp64 wave and block sums ---------------------------------------
 
+// DPP controls (gfx9 encoding): quad permutations [1,0,3,2] and [2,3,0,1]
+// (partners 1 and 2 apart), rotations by 4 and 8 lanes within a row of 16.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+// x of another lane by DPP control CTRL (both 32-bit halves moved alike).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x)
+{
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// x of lane `lane` (uniform).
+__device__ __forceinline__ double lane_f64(double x, int lane)
+{
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), lane));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), lane));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// The sum of q over the 64 lanes of a full wave, in a fixed order: each quad
+// adds partners 1 then 2 apart, each row of 16 adds the quad sums 4 then 8
+// lanes on (lane 0 of a row then holds the row's sum), and the rows' sums
+// are added in order 0, 1, 2, 3.  The result is uniform.  DPP moves and lane
+// reads keep the reduction out of LDS: with the ds_bpermute butterfly of
+// __shfl_xor the 8-slice clip pass at 256 threads took 2.78 instead of
+// 2.61 ms.
+__device__ __forceinline__ double wave_sum(double q)
+{
+    q = q + dpp_f64<kDppQuadXor1>(q);
+    q = q + dpp_f64<kDppQuadXor2>(q);
+    q = q + dpp_f64<kDppRowRor4>(q);
+    q = q + dpp_f64<kDppRowRor8>(q);
+    return ((lane_f64(q, 0) + lane_f64(q, 16)) + lane_f64(q, 32)) + lane_f64(q, 48);
+}
+
+// The block's sum of q, valid in thread 0: the wave sums, then wave by wave
+// in order.  Every thread of the block must call it.
 template <int BS>
 __device__ __forceinline__ double block_sum(double q)
 {
-    // xor butterfly: both partners add the same two values, so every lane
-    // ends with the same bits.
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) q = q + __shfl_xor(q, off, 64);
+    q = wave_sum(q);
     __shared__ double wave_sums[BS / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) wave_sums[wave] = q;
@@ -404,31 +474,41 @@ __device__ __forceinline__ double block_sum(double q)
 
 // ---- kernels ----------------------------------------------------------------------
 
-// A full block in the contiguous lane mapping (one vector's worth of
-// elements per thread); adds the thread's squares to q.
-template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
+// A full block of BS threads in the contiguous lane mapping (one vector's
+// worth of elements per thread); adds the thread's squares to q.  Loads go
+// through buffer resources over the block's tile of each slice (and of the
+// accumulator), and the reduced values are stored before any square is
+// formed: together with the DPP wave sum this took the 8-slice pass at 256
+// threads from 2.78 to 2.61 ms (64-bit global loads with the same code: 2.77).
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC, int BS>
 __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t base, double& q)
 {
     constexpr bool kF32 = std::is_same<GT, float>::value;
-    // f32x4 indices of this lane's two groups of four elements
-    const int64_t i0 = 2 * base + (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
-    const int64_t i1 = i0 + 64;
+    constexpr uint32_t kTile = static_cast<uint32_t>(BS) * 8;       // elements per block
+    constexpr int kGBytes = kF32 ? 4 : 2;
+    // this lane's two groups of four elements in the block's tile: f32x4
+    // index r0 and r0 + 64 (u32x2 index for bf16)
+    const uint32_t r0 = (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
+    // the block's tile of the reduced gradient (an accumulator is always stored)
+    auto mean_tile = [&]() { return buffer_rsrc(a.mean_out + base * 8, kTile * 4); };
     f32x4 c0{}, c1{};
     if constexpr (ACC != kAccNone) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(a.mean_out);
-        c0 = load<true>(p + i0);
-        c1 = load<true>(p + i1);
+        c0 = buffer_load_f4<kCpolNt>(mean_tile(), r0 * 16);
+        c1 = buffer_load_f4<kCpolNt>(mean_tile(), r0 * 16 + 1024);
     }
     float g[8];
     reduce_fetched<GT, NDT, WEIGHTED>(
         a,
         [&](int r) {
+            const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(
+                const_cast<char*>(static_cast<const char*>(a.slices.p[r])) + base * 8 * kGBytes,
+                kTile * kGBytes);
             if constexpr (kF32) {
-                const f32x4* q4 = static_cast<const f32x4*>(a.slices.p[r]);
-                return typename SliceIO<float>::Raw{load<true>(q4 + i0), load<true>(q4 + i1)};
+                return typename SliceIO<float>::Raw{buffer_load_f4<kCpolNt>(sr, r0 * 16),
+                                                    buffer_load_f4<kCpolNt>(sr, r0 * 16 + 1024)};
             } else {
-                const u32x2* q2 = static_cast<const u32x2*>(a.slices.p[r]);
-                const u32x2 lo = load<true>(q2 + i0), hi = load<true>(q2 + i1);
+                const u32x2 lo = buffer_load_u2<kCpolNt>(sr, r0 * 8);
+                const u32x2 hi = buffer_load_u2<kCpolNt>(sr, r0 * 8 + 512);
                 return u32x4{lo.x, lo.y, hi.x, hi.y};
             }
         },
@@ -439,13 +519,10 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
         for (int j = 0; j < 8; ++j) g[j] = accumulate1<ACC>(a, ac[j], g[j]);
     }
     if constexpr (STORE) {
-        const __amdgpu_buffer_rsrc_t mr =
-            buffer_rsrc(a.mean_out + base * 8, static_cast<uint32_t>(kSqVecPerBlock * 32));
-        buffer_store_f4<kCpolNt>(mr, static_cast<uint32_t>((i0 - 2 * base) * 16),
-                                 f32x4{g[0], g[1], g[2], g[3]});
-        buffer_store_f4<kCpolNt>(mr, static_cast<uint32_t>((i1 - 2 * base) * 16),
-                                 f32x4{g[4], g[5], g[6], g[7]});
+        buffer_store_f4<kCpolNt>(mean_tile(), r0 * 16, f32x4{g[0], g[1], g[2], g[3]});
+        buffer_store_f4<kCpolNt>(mean_tile(), r0 * 16 + 1024, f32x4{g[4], g[5], g[6], g[7]});
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const double d = g[j];
@@ -455,23 +532,25 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
 
 // Clip pass 1: the reduced gradient of the slices (optionally stored, or
 // accumulated over micro-batches) and one fp64 partial sum of its squares
-// per block.  Block span s (see block_span) owns kSqVecPerBlock consecutive
-// vectors; lane l of the block's wave w takes elements 4l..4l+3 and
+// per block.  Block span s (see block_span) owns BS consecutive vectors;
+// lane l of the block's wave w takes elements 4l..4l+3 and
 // 256+4l..256+4l+3 of the wave's 512 (the contiguous lane mapping).  A thread
 // adds its squares in a fixed order, and only the last block of a shard,
 // which meets the partial vector or runs past valid_len, takes the guarded
 // path (vector by vector, then element by element).
-template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
-__global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC, int BS>
+__global__ void __launch_bounds__(BS) k_reduce_sqnorm(const SqArgs a)
 {
     static_assert(STORE || ACC == kAccNone, "an accumulator is always stored");
-    static_assert(kSqThreads % 64 == 0, "whole waves");
+    static_assert(BS % 64 == 0 && BS >= kSqThreadsMin, "whole waves; workspace sized for the smallest");
     const int64_t nfull = a.valid_len >> 3;
-    const int64_t span = block_span(blockIdx.x, gridDim.x, a.xcd_contiguous != 0);
-    const int64_t base = a.v0 + span * kSqVecPerBlock;
+    // the wide shape maps blocks XCD-contiguously (a compile-time choice, so
+    // a wave issues its scalar loads without first waiting on a flag)
+    const int64_t span = block_span(blockIdx.x, gridDim.x, BS == kSqWideThreads);
+    const int64_t base = a.v0 + span * BS;
     double q = 0.0;
-    if (base + kSqVecPerBlock <= nfull) {
-        reduce_block_contiguous<GT, NDT, STORE, WEIGHTED, ACC>(a, base, q);
+    if (base + BS <= nfull) {
+        reduce_block_contiguous<GT, NDT, STORE, WEIGHTED, ACC, BS>(a, base, q);
     } else {
         const int64_t vi = base + threadIdx.x;
         if (vi < nfull) {
@@ -504,7 +583,7 @@ __global__ void __launch_bounds__(kSqThreads) k_reduce_sqnorm(const SqArgs a)
         }
     }
     if (a.partials) {   // uniform: every thread of the block takes the same branch
-        const double t = block_sum<kSqThreads>(q);
+        const double t = block_sum<BS>(q);
         if (threadIdx.x == 0) a.partials[span] = t;
     }
 }
@@ -814,20 +893,35 @@ int lds_reservation(int per_cu, size_t* bytes)
 // only makes the per-device set-up calls its kernel needs (prepare_kernels).
 constexpr int64_t kPrepareOnly = 0;
 
+template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC, int BS>
+int launch_reduce_bs(const SqArgs& a, int per_cu, int64_t blocks, hipStream_t st)
+{
+    size_t lds = 0;
+    const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC, BS>>(per_cu, &lds);
+    if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
+    hipLaunchKernelGGL((k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC, BS>), dim3(blocks), dim3(BS),
+                       lds, st, a);
+    return launched();
+}
+
+// The launch shape of sq_shape: fixed for a specialized N_d, chosen per call
+// for the generic kernel.
 template <typename GT, int NDT, bool STORE, bool WEIGHTED, int ACC>
 int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
 {
-    size_t lds = 0;
-    // fp32 slices (16 loads per thread at N_d = 8), accumulation passes
-    // (the accumulator's loads on top) and wide bf16 reductions keep enough
-    // bytes in flight at one block per CU
-    const bool wide = std::is_same<GT, float>::value || ACC != kAccNone || a.n_d >= kSqWideNd;
-    const int per_cu = wide ? kSqWidePerCu : kSqPerCu;
-    const int rc = lds_reservation<k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>>(per_cu, &lds);
-    if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
-    hipLaunchKernelGGL((k_reduce_sqnorm<GT, NDT, STORE, WEIGHTED, ACC>), dim3(blocks),
-                       dim3(kSqThreads), lds, st, a);
-    return launched();
+    constexpr bool kF32 = std::is_same<GT, float>::value;
+    if constexpr (NDT > 0) {
+        constexpr SqShape sh = sq_shape(NDT, kF32, ACC);
+        return launch_reduce_bs<GT, NDT, STORE, WEIGHTED, ACC, sh.threads>(a, sh.per_cu, blocks,
+                                                                           st);
+    } else {
+        const SqShape sh = sq_shape(a.n_d, kF32, ACC);
+        if (sh.threads == kSqWideThreads)
+            return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqWideThreads>(a, sh.per_cu,
+                                                                                blocks, st);
+        return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqThreadsMin>(a, sh.per_cu, blocks,
+                                                                           st);
+    }
 }
 
 // The bf16 mean, specialized for the common N_d.
@@ -996,19 +1090,23 @@ int prepare_device()
 
 // ---- the passes, as the C-ABI entry points enqueue them -----------------------------
 
+int64_t reduce_blocks(int64_t valid_len, int32_t n_d, bool f32, int acc)
+{
+    return sq_blocks(valid_len, sq_shape(n_d, f32, acc).threads);
+}
+
 int enqueue_reduce(SqArgs a, bool f32, bool weighted, int acc, bool store, double* partials,
                    void* stream)
 {
-    // block-to-data mapping (see block_span)
-    a.xcd_contiguous = a.n_d >= kSqWideNd ? 1 : 0;
     const bool general = f32 || weighted || acc != kAccNone;
-    const int64_t blocks = sq_blocks(a.valid_len);
+    const SqShape sh = sq_shape(a.n_d, f32, acc);
+    const int64_t blocks = sq_blocks(a.valid_len, sh.threads);
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();   // drop an error left by an unrelated earlier call
-    constexpr int64_t cap = max_blocks(kSqThreads);
+    const int64_t cap = max_blocks(sh.threads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-        a.v0 = b0 * kSqVecPerBlock;
+        a.v0 = b0 * sh.threads;
         a.partials = partials ? partials + b0 : nullptr;
         const int rc = general ? launch_reduce(a, f32, weighted, acc, nb, st)
                                : launch_sqnorm(a, store, nb, st);

@@ -73,8 +73,9 @@ def test_noalloc_equals_workspace_call_in_decreasing_sizes():
 
 def test_noalloc_at_its_largest_shard():
     """The largest shard the static array serves (2,146,959,360 parameters,
-    524,160 clip-pass blocks) gives the workspace call's squared norm bit for
-    bit; one vector more is rejected before anything is enqueued."""
+    1,048,320 clip-pass blocks of 256 threads) gives the workspace call's
+    squared norm bit for bit; one vector more is rejected before anything is
+    enqueued."""
     vmax = 2_146_959_360
     s = Z.zs_layout(vmax, 1, 0, 8, 0)
     assert Z.zs_workspace_bytes(s) == Z.ZS_SCRATCH_BYTES
