@@ -148,11 +148,14 @@ def bench_lib():
     return lib
 
 
-def step_pattern_ceiling(torch, run, reps=10):
+def step_pattern_without_arithmetic(torch, run, reps=10):
     """The step's access pattern without its arithmetic (k_step_pattern), on
     the arrays of the workload's first unit: fp32 gradient, w, m, v in, w, m,
-    v and the bf16 slot out, over the first multiple of 2048 parameters, at
-    two and at one resident block per CU.  GB/s at 30 bytes per parameter.
+    v and the bf16 slot out, over the first multiple of 2048 parameters, in
+    one-wave blocks at six (the step's residency) and at four per CU.  GB/s
+    at 30 bytes per parameter.  It shows whether the step's arithmetic costs
+    time: at the step's residency the step runs as fast as these accesses
+    alone, or faster (its arithmetic spaces out the requests).
     Only for steps that read a stored fp32 gradient and stream (the pattern
     of the dominant kernel there); runs after the timed region and leaves the
     state changed."""
@@ -164,7 +167,7 @@ def step_pattern_ceiling(torch, run, reps=10):
     out = d.out.data_ptr() + 2 * (run.shard.shard_offset if run.wl.out_mode == "gather" else 0)
     st = torch.cuda.current_stream()
     res = {}
-    for per_cu in (2, 1):
+    for per_cu in (6, 4):
         args = (d.mean.data_ptr(), d.w.data_ptr(), d.m.data_ptr(), d.v.data_ptr(), out, n,
                 per_cu, st.cuda_stream)
         assert lib.zs_bench_step_pattern(*args) == 0
@@ -364,7 +367,7 @@ def main():
     if ms_per_step < 1.0:
         out["graph_replay"] = graph_replay(torch, run, t, K)
     if not args.no_copy_ceiling:
-        pattern = step_pattern_ceiling(torch, run) if (run.store_mean and kname.startswith(
+        pattern = step_pattern_without_arithmetic(torch, run) if (run.store_mean and kname.startswith(
             "k_step") and launch_bytes >= (512 << 20)) else None
         del run
         torch.cuda.empty_cache()
@@ -374,7 +377,7 @@ def main():
                   "kernels_whole_step_over_copy": (red_b + upd_b) / ((red_ms + upd_ms) / 1e3)
                   / 1e9 / cc["gbps"]}
         if pattern is not None:
-            out["step_pattern_ceiling"] = pattern
+            out["step_pattern_without_arithmetic"] = pattern
             ratios["k_step_over_step_pattern"] = achieved / pattern["gbps"]
             ratios["step_pattern_over_copy"] = pattern["gbps"] / cc["gbps"]
         out["ceiling_ratios"] = ratios

@@ -38,8 +38,8 @@ extern "C" int zs_bench_copy(const void* src, void* dst, int64_t n16, int32_t bl
 }
 
 // The step's memory pattern without its arithmetic: the accesses of a full
-// block of the streaming optimizer step (256 threads, each lane the f32x4
-// groups q0 and q0 + 64 of its wave's 512 parameters; non-temporal loads of
+// block of the streaming optimizer step (one wave, each lane the f32x4
+// groups q0 and q0 + 64 of the wave's 512 parameters; non-temporal loads of
 // the fp32 gradient, w, m and v; stores of w, m, v and the bf16 parameters
 // through buffer resources with sc1 and nt), with three additions per
 // element in place of AdamW.  Its time is the ceiling the step's access
@@ -50,7 +50,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(void* base, uint32_t
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
 }
 
-constexpr int kPatThreads = 256;
+constexpr int kPatThreads = 64;
 constexpr int kPatTile = kPatThreads * 8;   // parameters per block
 constexpr int kSc1Nt = 16 | 2;
 
@@ -89,8 +89,8 @@ __global__ void __launch_bounds__(kPatThreads)
     __builtin_amdgcn_raw_buffer_store_b64(hi2(w1), ro, b1 / 2, 0, kSc1Nt);
 }
 
-// n parameters (a positive multiple of 2048, below 2^31 * 8 / 256 blocks'
-// worth); g, w, m, v: device fp32[n], out: device bf16[n], 16-byte aligned.
+// n parameters (a positive multiple of 512, fewer than 2^31 threads' worth);
+// g, w, m, v: device fp32[n], out: device bf16[n], 16-byte aligned.
 // per_cu: resident blocks per CU enforced by a dynamic LDS reservation (0:
 // no cap).  Returns 0, or -1 (arguments), -5 (alignment), -11 (launch).
 extern "C" int zs_bench_step_pattern(const float* g, float* w, float* m, float* v,

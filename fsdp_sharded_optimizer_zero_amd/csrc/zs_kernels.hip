@@ -55,25 +55,31 @@ namespace {
 // (interleaved repeats in one process, the workloads' real sizes).
 //
 // Threads per block of the step and the pack; each thread owns one
-// 8-parameter vector.  The clip pass's shape is in zs_internal.h because the
-// workspace size depends on it.
-constexpr int kStepThreads = 256;
+// 8-parameter vector.  The step runs one-wave blocks: a CU slot frees as soon
+// as its one wave is done, not when the slowest wave of a larger block is.
+constexpr int kStepThreads = 64;
 constexpr int64_t kStepVecPerBlock = kStepThreads;
 // Blocks of the step / of the clip pass that may be resident on one CU at a
 // time.  A dynamic LDS reservation enforces the cap.  Few resident waves keep
 // the window of addresses in flight narrow, which suits the HBM better than a
-// full CU when 4 to 65 arrays stream at once.  The step takes 4.39 ms on an
-// 872M-parameter shard at two 256-thread blocks per CU, 5.10 at one (its
-// division and square-root chain exposed), 4.60 at three, 4.84 uncapped;
-// 512-thread blocks at one per CU, or 2 or 4 vectors per thread, 4.62-4.83.
-// The clip pass's shape is sq_shape below.
-constexpr int kStepPerCu = 2;
+// full CU when 4 to 65 arrays stream at once.  The step runs six one-wave
+// blocks per CU: 4.11 ms on the 875M-parameter shard against 4.26 at two
+// 256-thread blocks (the same shard, interleaved), 4.16 and 4.56 at five
+// and four (its division and square-root chain exposed), 4.15-4.50 at 7-12;
+// 4.98 against 5.34 ms on the 1.09B shard; 128- or 192-thread blocks and 2
+// or 4 vectors per thread were slower.  The clip pass's shape is sq_shape
+// below.
+constexpr int kStepPerCu = 6;
 // Launch shape of the clip pass.  A bf16 reduction of kSqWideNd slices or
 // more keeps enough loads in flight per thread to run 512-thread blocks at
 // one per CU (64 slices of 1.09B: 22.4 ms, against 22.5 ms at two 256-thread
-// blocks); every other reduction runs 256-thread blocks at two per CU (8
-// bf16 slices of 875M: 2.61 ms, against 2.82 ms at two 512-thread blocks).
-// The workspace is sized for 256-thread blocks (kSqThreadsMin).
+// blocks); fp32 slices, with twice the bytes in flight per thread, run
+// 256-thread blocks at one per CU (8 slices of 875M: 5.19 ms, against 5.45 at
+// two and 5.47 at one 512-thread block); every other reduction runs
+// 256-thread blocks at two per CU (8 bf16 slices: 2.71 ms, against 2.84 ms
+// at two 512-thread blocks; 4 accumulation passes 12.72 ms, against 12.91 at
+// one 512-thread block and 14.13 at one 256-thread block).  The workspace is
+// sized for 256-thread blocks (kSqThreadsMin).
 constexpr int kSqWideNd = 32;
 // The wide shape also maps blocks XCD-contiguously (see block_span).
 constexpr int kSqWideThreads = 512;
@@ -82,8 +88,9 @@ struct SqShape {
 };
 constexpr SqShape sq_shape(int32_t n_d, bool f32, int acc)
 {
-    return (!f32 && acc == kAccNone && n_d >= kSqWideNd) ? SqShape{kSqWideThreads, 1}
-                                                          : SqShape{kSqThreadsMin, 2};
+    if (f32) return SqShape{kSqThreadsMin, 1};
+    return (acc == kAccNone && n_d >= kSqWideNd) ? SqShape{kSqWideThreads, 1}
+                                                 : SqShape{kSqThreadsMin, 2};
 }
 // Gradient slices whose loads one thread has in flight at once; the wide
 // specializations (N_d >= kSqWideNd, one block per CU) keep fewer in flight

@@ -9,9 +9,9 @@ per launch of the step and of the clip pass.  Shards of 1-2 million
 parameters with a ragged tail then cross several launch boundaries (the last
 launch of the 64-slice clip pass has 13 blocks, so the XCD-contiguous block
 mapping meets a grid that is not a multiple of 8).  The test build also takes
-the step's streaming loads (non-temporal gradient and v) at every size, which
-the normal build uses only for steps that move 2 GiB or more: the comparison
-with the normal build covers both load policies.
+the step's streaming cache policy (non-temporal loads, sc1 and nt stores) at
+every size, which the normal build uses only for steps that move 512 MiB or
+more: the comparison with the normal build covers both policies.
 
 Each output must equal the oracle's bit for bit (the squared norm within the
 oracle's bar, Q_REL_BAR), equal the normal build's bit for bit, and leave

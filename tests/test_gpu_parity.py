@@ -657,9 +657,9 @@ DEGENERATE = [
 
 @pytest.mark.parametrize("name,kw", DEGENERATE, ids=[d[0] for d in DEGENERATE])
 def test_degenerate_hyperparameters(name, kw):
-    """Every schedule against the oracle on a ragged 5,000-parameter shard (two
-    full blocks of the step and a partial one), at hyperparameters where the
-    arithmetic degenerates."""
+    """Every schedule against the oracle on a ragged 5,000-parameter shard
+    (full blocks of the step and the clip pass, then a partial one), at
+    hyperparameters where the arithmetic degenerates."""
     psi, n_d, rank = 4 * 5000 + 3, 4, 3
     base = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=7,
                 max_grad_norm=0.0)
