@@ -103,11 +103,11 @@ constexpr int kRedGroupWide = 4;
 //  - The clip pass loads and stores nt (plain loads: 3.03 vs 2.80 ms at 8
 //    slices, 23.5 vs 22.6 ms at 64; plain stores 3.05 and 23.4 ms).
 //  - The step's full blocks store with sc1 and nt when the step streams (see
-//    kStepStreamBytes): 4.34 vs 4.41 ms with nt alone on an 872M-parameter
-//    shard, 4.90 with plain stores; the same write pattern without the
-//    arithmetic gains as much (4.39 vs 4.48 ms).  sc0 on top, or sc1 without
-//    nt, gains nothing.  Load policies (nt, sc0, sc1 in any combination) make
-//    no difference to either pass.
+//    kStepStreamBytes): 4.10 vs 4.30 ms with nt alone on the 875M-parameter
+//    shard, 5.18 vs 5.59 ms on the 1.09B one, 4.03 vs 4.17 ms for 32 FSDP
+//    units; plain stores were slower still (4.90 vs 4.41 ms at 256-thread
+//    blocks).  sc0 on top, or sc1 without nt, gains nothing.  Load policies
+//    (nt, sc0, sc1 in any combination) make no difference to either pass.
 constexpr int kCpolNt = 2;
 constexpr int kCpolSc1Nt = 16 | 2;
 // A step that moves at least this many bytes -- twice the 256 MB Infinity
