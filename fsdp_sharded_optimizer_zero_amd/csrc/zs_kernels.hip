@@ -55,21 +55,24 @@ namespace {
 // (interleaved repeats in one process, the workloads' real sizes).
 //
 // Threads per block of the step and the pack; each thread owns one
-// 8-parameter vector.  The step runs one-wave blocks: a CU slot frees as soon
-// as its one wave is done, not when the slowest wave of a larger block is.
-constexpr int kStepThreads = 64;
-constexpr int64_t kStepVecPerBlock = kStepThreads;
+// 8-parameter vector.  A streaming step (see kStepStreamBytes) runs one-wave
+// blocks: a CU slot frees as soon as its one wave is done, not when the
+// slowest wave of a larger block is.  A smaller step, whose operands the
+// Infinity Cache partly holds from one step to the next, runs 256-thread
+// blocks (15.6M parameters: 72 us, against 78 us in one-wave blocks).
+constexpr int step_threads(bool stream) { return stream ? 64 : 256; }
+constexpr int kPackThreads = 256;
 // Blocks of the step / of the clip pass that may be resident on one CU at a
 // time.  A dynamic LDS reservation enforces the cap.  Few resident waves keep
 // the window of addresses in flight narrow, which suits the HBM better than a
-// full CU when 4 to 65 arrays stream at once.  The step runs six one-wave
-// blocks per CU: 4.11 ms on the 875M-parameter shard against 4.26 at two
-// 256-thread blocks (the same shard, interleaved), 4.16 and 4.56 at five
-// and four (its division and square-root chain exposed), 4.15-4.50 at 7-12;
-// 4.98 against 5.34 ms on the 1.09B shard; 128- or 192-thread blocks and 2
-// or 4 vectors per thread were slower.  The clip pass's shape is sq_shape
-// below.
-constexpr int kStepPerCu = 6;
+// full CU when 4 to 65 arrays stream at once.  A streaming step runs six
+// one-wave blocks per CU: 4.11 ms on the 875M-parameter shard against 4.26
+// at two 256-thread blocks (the same shard, interleaved), 4.16 and 4.56 at
+// five and four (its division and square-root chain exposed), 4.15-4.50 at
+// 7-12; 4.98 against 5.34 ms on the 1.09B shard; 128- or 192-thread blocks
+// and 2 or 4 vectors per thread were slower.  A smaller step runs two
+// 256-thread blocks per CU.  The clip pass's shape is sq_shape below.
+constexpr int step_per_cu(bool stream) { return stream ? 6 : 2; }
 // Launch shape of the clip pass.  A bf16 reduction of kSqWideNd slices or
 // more keeps enough loads in flight per thread to run 512-thread blocks at
 // one per CU (64 slices of 1.09B: 22.4 ms, against 22.5 ms at two 256-thread
@@ -693,7 +696,8 @@ __device__ __forceinline__ void step_arith(const StepArgs& a, const float (&g)[8
 template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t base)
 {
-    static_assert(kStepThreads % 64 == 0, "whole waves");
+    constexpr int kThreads = step_threads(STREAM);
+    static_assert(kThreads % 64 == 0, "whole waves");
     constexpr int CPOL = STREAM ? kCpolSc1Nt : kCpolNt;
     const int64_t r0 = (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);   // in the block's tile
     const int64_t q0 = 2 * base + r0;
@@ -724,9 +728,9 @@ __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t
     float M[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
     float V[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     step_arith<CLIP>(a, g, W, M, V);
-    // the block's tile: kStepVecPerBlock * 32 bytes of each fp32 array, half
-    // that of the bf16 slot; the lane's byte offsets in it
-    constexpr uint32_t kTile = static_cast<uint32_t>(kStepVecPerBlock * 32);
+    // the block's tile: kThreads vectors, 32 bytes each of every fp32 array,
+    // half that of the bf16 slot; the lane's byte offsets in it
+    constexpr uint32_t kTile = static_cast<uint32_t>(kThreads * 32);
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + base * 8, kTile);
     const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(a.m + base * 8, kTile);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + base * 8, kTile);
@@ -780,7 +784,7 @@ __device__ __forceinline__ void step_vector(const StepArgs& a, int64_t vi)
 // The fused step over the slot's shard_len/8 vectors: gradient (mean of the
 // slices, or the stored mean), clip, AdamW in place, bf16 cast into the
 // slot; vectors past valid_len are pads and get +0.  Block b of a launch
-// owns kStepVecPerBlock consecutive vectors.
+// owns step_threads(STREAM) consecutive vectors (one per thread).
 // Full blocks take the contiguous lane mapping (step_block_contiguous):
 // measured against the plain one on MI355X (interleaved medians, one box),
 // 4.40 vs 4.47 ms for 875M parameters, 5.33 vs 5.51 ms for 1.09B, 70 vs 75 us
@@ -794,12 +798,13 @@ __device__ __forceinline__ void step_vector(const StepArgs& a, int64_t vi)
 // steps find partly in the 256 MB Infinity Cache, loses (74 vs 70 us), so
 // the host picks STREAM from the bytes the step moves (kStepStreamBytes).
 template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
-__global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
+__global__ void __launch_bounds__(step_threads(STREAM)) k_step(const StepArgs a)
 {
     const int64_t nfull = a.valid_len >> 3;
     const int64_t nslot = a.shard_len >> 3;
-    const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kStepVecPerBlock;
-    if (base + kStepVecPerBlock <= nfull) {
+    constexpr int64_t kVecs = step_threads(STREAM);
+    const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kVecs;
+    if (base + kVecs <= nfull) {
         step_block_contiguous<FROM_SLICES, NDT, CLIP, STREAM>(a, base);
         return;
     }
@@ -823,10 +828,10 @@ __global__ void __launch_bounds__(kStepThreads) k_step(const StepArgs a)
 }
 
 // Cast and pack only: vector vi of the slot, one per thread.
-__global__ void __launch_bounds__(kStepThreads)
+__global__ void __launch_bounds__(kPackThreads)
     k_pack(const float* w, uint16_t* out, int64_t valid_len, int64_t shard_len, int64_t v0)
 {
-    const int64_t vi = v0 + static_cast<int64_t>(blockIdx.x) * kStepThreads + threadIdx.x;
+    const int64_t vi = v0 + static_cast<int64_t>(blockIdx.x) * kPackThreads + threadIdx.x;
     const int64_t nfull = valid_len >> 3;
     if (vi < nfull) {
         const f32x4* w4 = reinterpret_cast<const f32x4*>(w);
@@ -1008,10 +1013,11 @@ template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
 int launch_step_k(const StepArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
-    const int rc = lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(kStepPerCu, &lds);
+    const int rc =
+        lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(step_per_cu(STREAM), &lds);
     if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
     hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, CLIP, STREAM>), dim3(blocks),
-                       dim3(kStepThreads), lds, st, a);
+                       dim3(step_threads(STREAM)), lds, st, a);
     return launched();
 }
 
@@ -1131,17 +1137,19 @@ int enqueue_sqnorm_sums(double* partials, int64_t blocks, int32_t units, double*
 
 int enqueue_step(StepArgs a, bool from_slices, bool clip, void* stream)
 {
-    const int64_t blocks = ((a.shard_len >> 3) + kStepVecPerBlock - 1) / kStepVecPerBlock;
+    const int64_t nvec = a.shard_len >> 3;
     // bytes the whole step moves: gradient in, state in and out, bf16 out
     const int64_t step_bytes =
         a.valid_len * (from_slices ? 2 * static_cast<int64_t>(a.n_d) + 26 : 30);
     const bool stream_loads = step_bytes >= kStepStreamBytes;
+    const int threads = step_threads(stream_loads);
+    const int64_t blocks = (nvec + threads - 1) / threads;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    constexpr int64_t cap = max_blocks(kStepThreads);
+    const int64_t cap = max_blocks(threads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-        a.v0 = b0 * kStepVecPerBlock;
+        a.v0 = b0 * threads;
         const int rc = launch_step(a, from_slices, clip, stream_loads, nb, st);
         if (rc != ZS_OK) return rc;
     }
@@ -1151,14 +1159,14 @@ int enqueue_step(StepArgs a, bool from_slices, bool clip, void* stream)
 int enqueue_pack(const float* master, uint16_t* out, int64_t valid_len, int64_t shard_len,
                  void* stream)
 {
-    const int64_t blocks = ((shard_len >> 3) + kStepThreads - 1) / kStepThreads;
+    const int64_t blocks = ((shard_len >> 3) + kPackThreads - 1) / kPackThreads;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    constexpr int64_t cap = max_blocks(kStepThreads);
+    constexpr int64_t cap = max_blocks(kPackThreads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-        hipLaunchKernelGGL(k_pack, dim3(nb), dim3(kStepThreads), 0, st, master, out, valid_len,
-                           shard_len, b0 * kStepThreads);
+        hipLaunchKernelGGL(k_pack, dim3(nb), dim3(kPackThreads), 0, st, master, out, valid_len,
+                           shard_len, b0 * kPackThreads);
         const int rc = launched();
         if (rc != ZS_OK) return rc;
     }
