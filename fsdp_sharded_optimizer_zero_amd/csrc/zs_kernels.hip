@@ -95,6 +95,8 @@ constexpr SqShape sq_shape(int32_t n_d, bool f32, int acc)
     return (acc == kAccNone && n_d >= kSqWideNd) ? SqShape{kSqWideThreads, 1}
                                                  : SqShape{kSqThreadsMin, 2};
 }
+static_assert(kSqWideThreads % 64 == 0 && kSqWideThreads > kSqThreadsMin,
+              "the generic kernel is instantiated for these two block sizes only");
 // Gradient slices whose loads one thread has in flight at once; the wide
 // specializations (N_d >= kSqWideNd, one block per CU) keep fewer in flight
 // (64 slices of 1.09B: 24.04 vs 24.24 ms with 8, 24.75 with 3, 27.5 with 2;
@@ -927,12 +929,16 @@ int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
         return launch_reduce_bs<GT, NDT, STORE, WEIGHTED, ACC, sh.threads>(a, sh.per_cu, blocks,
                                                                            st);
     } else {
+        // the block size the caller sized the grid for (sq_shape gives one of
+        // these two)
         const SqShape sh = sq_shape(a.n_d, kF32, ACC);
         if (sh.threads == kSqWideThreads)
             return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqWideThreads>(a, sh.per_cu,
                                                                                 blocks, st);
-        return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqThreadsMin>(a, sh.per_cu, blocks,
-                                                                           st);
+        if (sh.threads == kSqThreadsMin)
+            return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqThreadsMin>(a, sh.per_cu,
+                                                                               blocks, st);
+        return ZS_ELAUNCH;
     }
 }
 
