@@ -34,7 +34,7 @@ ZS_EINVAL_REDUCE = -12
 ZS_EZERO_TOKENS = -13
 ZS_EINVAL_UNITS = -14
 ZS_ESCRATCH = -15
-ZS_SCRATCH_BYTES = 8 << 20
+ZS_SCRATCH_BYTES = 16 << 20
 ZS_GRAD_BF16 = 0
 ZS_GRAD_F32 = 1
 ZS_MAX_RANKS = 64

@@ -20,11 +20,11 @@ struct StepConsts {
     int32_t bc1_pow2, bc2_pow2;
 };
 
-// The clip pass runs blocks of 256 or 512 threads (one 8-parameter vector
-// per thread, the size chosen per call by the kernel part) and writes one
-// fp64 partial sum per block into the workspace; the workspace is sized for
-// the smaller block.
-constexpr int kSqThreadsMin = 256;
+// The clip pass runs blocks of 128, 256 or 512 threads (one 8-parameter
+// vector per thread, the size chosen per call by the kernel part) and writes
+// one fp64 partial sum per block into the workspace; the workspace is sized
+// for the smallest block.
+constexpr int kSqThreadsMin = 128;
 
 // Blocks of the clip pass over valid_len parameters at `threads` threads per
 // block (the last vector may be partial).

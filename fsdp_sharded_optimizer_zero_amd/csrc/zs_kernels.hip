@@ -75,28 +75,31 @@ constexpr int kPackThreads = 256;
 constexpr int step_per_cu(bool stream) { return stream ? 6 : 2; }
 // Launch shape of the clip pass.  A bf16 reduction of kSqWideNd slices or
 // more keeps enough loads in flight per thread to run 512-thread blocks at
-// one per CU (64 slices of 1.09B: 22.4 ms, against 22.5 ms at two 256-thread
-// blocks); fp32 slices, with twice the bytes in flight per thread, run
-// 256-thread blocks at one per CU (8 slices of 875M: 5.19 ms, against 5.45 at
-// two and 5.47 at one 512-thread block); every other reduction runs
-// 256-thread blocks at two per CU (8 bf16 slices: 2.71 ms, against 2.84 ms
-// at two 512-thread blocks; 4 accumulation passes 12.72 ms, against 12.91 at
-// one 512-thread block and 14.13 at one 256-thread block).  The workspace is
-// sized for 256-thread blocks (kSqThreadsMin).
+// one per CU (64 slices of 1.09B: 24.1 ms, against 25.0 at two per CU, 25.3
+// at one 1024-thread block, 27.7-34.1 ms in blocks of 64 to 256 threads);
+// fp32 slices, with twice the bytes in flight per thread, run 128-thread
+// blocks at two per CU (8 slices of 875M: 5.05 ms, against 5.18 at one
+// 256-thread block, 5.13 at four one-wave blocks, 5.23 at three 128-thread
+// blocks, 5.44 at two 256-thread blocks, 6.24 at one 128-thread block);
+// every other reduction runs 256-thread blocks at two per CU (8 bf16 slices:
+// 2.71 ms, against 2.84 ms at two 512-thread blocks; 4 accumulation passes
+// 12.72 ms, against 12.91 at one 512-thread block and 14.13 at one 256-thread
+// block).  The workspace is sized for the smallest block (kSqThreadsMin).
 constexpr int kSqWideNd = 32;
 // The wide shape also maps blocks XCD-contiguously (see block_span).
 constexpr int kSqWideThreads = 512;
+constexpr int kSqThreads = 256;
 struct SqShape {
     int threads, per_cu;
 };
 constexpr SqShape sq_shape(int32_t n_d, bool f32, int acc)
 {
-    if (f32) return SqShape{kSqThreadsMin, 1};
+    if (f32) return SqShape{kSqThreadsMin, 2};
     return (acc == kAccNone && n_d >= kSqWideNd) ? SqShape{kSqWideThreads, 1}
-                                                 : SqShape{kSqThreadsMin, 2};
+                                                 : SqShape{kSqThreads, 2};
 }
-static_assert(kSqWideThreads % 64 == 0 && kSqWideThreads > kSqThreadsMin,
-              "the generic kernel is instantiated for these two block sizes only");
+static_assert(kSqThreadsMin % 64 == 0 && kSqThreadsMin < kSqThreads && kSqThreads < kSqWideThreads,
+              "three block sizes, the workspace sized for the smallest");
 // Gradient slices whose loads one thread has in flight at once; the wide
 // specializations (N_d >= kSqWideNd, one block per CU) keep fewer in flight
 // (64 slices of 1.09B: 24.04 vs 24.24 ms with 8, 24.75 with 3, 27.5 with 2;
@@ -929,15 +932,21 @@ int launch_reduce_k(const SqArgs& a, int64_t blocks, hipStream_t st)
         return launch_reduce_bs<GT, NDT, STORE, WEIGHTED, ACC, sh.threads>(a, sh.per_cu, blocks,
                                                                            st);
     } else {
-        // the block size the caller sized the grid for (sq_shape gives one of
-        // these two)
+        // the block size the caller sized the grid for: fp32 slices take
+        // one shape, bf16 slices one of two
         const SqShape sh = sq_shape(a.n_d, kF32, ACC);
-        if (sh.threads == kSqWideThreads)
-            return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqWideThreads>(a, sh.per_cu,
+        if constexpr (kF32) {
+            if (sh.threads == kSqThreadsMin)
+                return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqThreadsMin>(a, sh.per_cu,
+                                                                                   blocks, st);
+        } else {
+            if (sh.threads == kSqWideThreads)
+                return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqWideThreads>(
+                    a, sh.per_cu, blocks, st);
+            if (sh.threads == kSqThreads)
+                return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqThreads>(a, sh.per_cu,
                                                                                 blocks, st);
-        if (sh.threads == kSqThreadsMin)
-            return launch_reduce_bs<GT, 0, STORE, WEIGHTED, ACC, kSqThreadsMin>(a, sh.per_cu,
-                                                                               blocks, st);
+        }
         return ZS_ELAUNCH;
     }
 }

@@ -95,7 +95,7 @@ extern "C" {
 #define ZS_MAX_RANKS 64          /* gradient slices one call can reduce */
 /* Bytes of the per-device static scratch array of shard_grad_sqnorm_noalloc:
  * the workspace of shards of up to 2,146,959,360 parameters. */
-#define ZS_SCRATCH_BYTES ((size_t)8 << 20)
+#define ZS_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* Where the new bf16 shard goes. */
 #define ZS_OUT_GATHER 0  /* param_out is the bf16[n_d * shard_len] all-gather
@@ -143,8 +143,8 @@ int zs_layout(int64_t psi, int32_t n_d, int32_t rank, int64_t align, int32_t sta
 /* Bytes of device workspace shard_grad_sqnorm needs for the squared norm of
  * "Data parallelism, ZeRO and FSDP", section 7 "Common mistakes" (global
  * clipping of sharded gradients): one fp64 partial sum
- * per block of its first pass (at most one block per 2048 parameters) plus
- * one per group of 4096 such partials, rounded up to 256 bytes -- 3.4 MB for
+ * per block of its first pass (at most one block per 1024 parameters) plus
+ * one per group of 4096 such partials, rounded up to 256 bytes -- 6.8 MB for
  * an 875M-parameter shard, at least 256 bytes (an empty shard).  Host only. */
 size_t zs_workspace_bytes(const zs_shard* s);
 
@@ -192,7 +192,7 @@ int shard_grad_sqnorm(const zs_shard* s, const uint16_t* const* grad_slices, flo
                       int32_t accumulate, void* stream);
 
 /* Bytes of device workspace shard_grad_sqnorm_units needs for `units`
- * units of layout s: units x what one shard needs (3.4 MB per 875M
+ * units of layout s: units x what one shard needs (6.8 MB per 875M
  * parameters of a unit).  Host only. */
 size_t zs_workspace_bytes_units(const zs_shard* s, int32_t units);
 
@@ -315,7 +315,7 @@ int shard_pack_gather(const zs_shard* s, const float* master, uint16_t* param_ou
  * capture, tight serving loops, harnesses that forbid hipMalloc): the clip
  * pass of shard_grad_sqnorm with the same arguments except the workspace,
  * computed by the same kernels into the same results bit for bit.  Its
- * block partials live in a static device array of ZS_SCRATCH_BYTES (8 MiB)
+ * block partials live in a static device array of ZS_SCRATCH_BYTES (16 MiB)
  * per device, held from the first use until the process ends; the call
  * itself allocates nothing and needs no zeroed memory.  Every call on one
  * device shares that device's array, so calls that overlap on one device

@@ -72,8 +72,9 @@ def test_noalloc_equals_workspace_call_in_decreasing_sizes():
 
 
 def test_noalloc_at_its_largest_shard():
-    """The largest shard the static array serves (2,146,959,360 parameters,
-    1,048,320 clip-pass blocks of 256 threads) gives the workspace call's
+    """The largest shard the static array serves (2,146,959,360 parameters:
+    room for the partials of 128-thread blocks, the smallest the clip pass
+    runs, and their group sums; this bf16 call runs 256-thread blocks) gives the workspace call's
     squared norm bit for bit; one vector more is rejected before anything is
     enqueued."""
     vmax = 2_146_959_360
