@@ -16,8 +16,7 @@ import fsdp_sharded_optimizer_zero_amd as Z
 import oracle as O
 from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
 from zsgen.workloads import NEXT, WORKLOADS
-from parity_util import (Q_REL_BAR, assert_bf16_close, assert_state_close, coef_is_robust,
-                         log, oracle_sampled_step, oracle_sqnorm_chunked, sample_indices)
+from parity_util import Q_REL_BAR, coef_is_robust, compare_unit_full, log, oracle_sqnorm_chunked
 from reduce_util import (F32_SENTINEL, GUARD, draw_slices, oracle_reduce, rows_on_device,
                          run_reduce_case)
 
@@ -105,7 +104,8 @@ def test_reduce_zero_tokens_rejects_and_writes_nothing():
 def test_next_workloads_full_size(name):
     """One optimizer step of the 7B ZeRO-2 shard with fp32 slices, token
     weights, or 4 accumulated micro-batches: the oracle's squared norm over
-    the whole shard, and the whole step at ~1M sampled positions."""
+    the whole shard, then every element of w, m, v, the bf16 slot and the
+    stored gradient against the oracle's step from its own gradient."""
     wl = WORKLOADS[name]
     log(f"{name}: allocating and filling on the device")
     run = ShardRun(wl)
@@ -116,21 +116,13 @@ def test_next_workloads_full_size(name):
     gq = float(run.sqnorm.item())
     V, s = run.V, run.shard
     log(f"{name}: GPU Q={gq:.6g}; oracle squared norm over {V:,} params")
-    oq = oracle_sqnorm_chunked(wl, 0, wl.t0, s.shard_offset, V)
+    oq, og = oracle_sqnorm_chunked(wl, 0, wl.t0, s.shard_offset, V, keep_all=True)
     log(f"{name}: oracle Q={oq:.17g} GPU Q={gq:.17g}")
     assert abs(gq - oq) <= Q_REL_BAR * oq
     coef = O.clip_coef(oq, wl.max_grad_norm)
-    idx = sample_indices(V, 1 << 20, seed=7)
-    ow, om, ov, oout, og = oracle_sampled_step(wl, 0, wl.t0, s, idx, coef)
+    nb = compare_unit_full(name, wl, run, 0, wl.t0, og, coef)
+    del og
     d = run.units_data[0]
-    ti = torch.from_numpy(idx).cuda()
-    nb = assert_state_close(f"{name} w", d.w[ti].cpu().numpy(), ow)
-    nb += assert_state_close(f"{name} m", d.m[ti].cpu().numpy(), om)
-    nb += assert_state_close(f"{name} v", d.v[ti].cpu().numpy(), ov)
-    nb += assert_bf16_close(f"{name} out",
-                            d.out[ti + s.shard_offset].cpu().numpy().view(np.uint16), oout)
-    gmean = d.mean[ti].cpu().numpy()
-    assert np.array_equal(gmean.view(np.uint32), og.view(np.uint32)), f"{name}: gradient bits"
     assert bool((d.out[:s.shard_offset] == 0x7FC1).all())
     assert bool((d.out[s.shard_offset + s.shard_len:] == 0x7FC1).all())
     if coef_is_robust(oq, wl.max_grad_norm):
