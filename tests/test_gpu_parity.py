@@ -245,10 +245,11 @@ def test_stage0_ddp_equals_concatenated_shards():
 
 def test_generic_nd_across_the_residency_threshold():
     """An N_d without a specialized kernel runs the generic one, whose clip
-    pass takes two blocks per CU below 32 slices and one from 32 up, with
-    twice the LDS reservation.  Both orders in one process: the larger
-    reservation after the smaller one on the same kernel, and back (the mean,
-    the token-weighted reduction and the step against the oracle)."""
+    pass runs 256-thread blocks at two per CU below 32 slices and 512-thread
+    blocks at one per CU (XCD-contiguous) from 32 up, the block size chosen
+    per call.  Both orders in one process: the wide shape after the narrow
+    one, and back (the mean, the token-weighted reduction and the step
+    against the oracle)."""
     from reduce_util import run_reduce_case
     rng = np.random.default_rng(48)
     for k, n_d in enumerate((3, 48, 5, 40)):
