@@ -161,51 +161,103 @@ def oracle_sqnorm_chunked(wl: Workload, unit: int, t: int, start: int, n: int,
     return q
 
 
-def compare_unit_full(name, wl: Workload, run, unit: int, t: int, g, coef,
-                      chunk: int = 1 << 24):
-    """Every element of one unit's step against the oracle: chunk by chunk,
-    the oracle's AdamW (O4, with the oracle's clip coefficient `coef`, None
-    for no clip) and bf16 pack (O5) from the oracle's gradient `g` (fp32[V],
-    from oracle_sqnorm_chunked(keep_all=True)) and the host generator's
-    initial state, against the device's w, m, v, gather slot and stored
-    gradient.  Asserts the fp32 and bf16 bars on every element and returns
-    the number of elements that are not bit-identical (all arrays)."""
-    s = run.shard
-    d = run.units_data[unit]
-    V, off = s.valid_len, s.shard_offset
-    base = off if wl.out_mode == "gather" else 0
-    h = hparams(wl, t)
-    nbit = {"w": 0, "m": 0, "v": 0, "out": 0, "gradient": 0}
-    worst = {"w": 0.0, "m": 0.0, "v": 0.0}
-    max_ulp = 0
-    for a in range(0, V, chunk):
-        n = min(chunk, V - a)
-        w, m, v = host_state(wl, unit, off + a, n)
-        gc = g[a:a + n]
-        O.adamw_f32(h, gc, w, m, v, coef=coef)
+class _FullCompare:
+    """Element-by-element comparison of one unit's step with the oracle,
+    chunk by chunk: the oracle's AdamW (O4, with the oracle's clip
+    coefficient, None for no clip) and bf16 pack (O5) from the oracle's
+    gradient of the chunk and the host generator's initial state, against the
+    device's w, m, v, output slot and stored gradient.  Asserts the fp32 and
+    bf16 bars on every element and counts the elements that are not
+    bit-identical."""
+
+    def __init__(self, name, wl: Workload, run, unit: int, t: int, coef):
+        self.name, self.wl, self.unit, self.coef = name, wl, unit, coef
+        s = run.shard
+        self.d = run.units_data[unit]
+        self.V, self.off = s.valid_len, s.shard_offset
+        self.base = self.off if wl.out_mode == "gather" else 0
+        self.h = hparams(wl, t)
+        self.nbit = {"w": 0, "m": 0, "v": 0, "out": 0, "gradient": 0}
+        self.worst = {"w": 0.0, "m": 0.0, "v": 0.0}
+        self.max_ulp = 0
+
+    def chunk(self, a: int, gc: np.ndarray):
+        name, d, n = self.name, self.d, len(gc)
+        w, m, v = host_state(self.wl, self.unit, self.off + a, n)
+        O.adamw_f32(self.h, gc, w, m, v, coef=self.coef)
         ob = O.bf16_rne(w)
         dev = {"w": d.w[a:a + n].cpu().numpy(), "m": d.m[a:a + n].cpu().numpy(),
                "v": d.v[a:a + n].cpu().numpy()}
         for k, ref in (("w", w), ("m", m), ("v", v)):
             e = rel_err(dev[k], ref)
-            worst[k] = max(worst[k], float(e.max()))
+            self.worst[k] = max(self.worst[k], float(e.max()))
             assert e.max() <= REL_BAR, f"{name} {k}[{a}:{a + n}]: max rel err {e.max()}"
-            nbit[k] += int(np.count_nonzero(dev[k].view(np.uint32) != ref.view(np.uint32)))
-        gout = d.out[base + a:base + a + n].cpu().numpy().view(np.uint16)
+            self.nbit[k] += int(np.count_nonzero(dev[k].view(np.uint32) != ref.view(np.uint32)))
+        gout = d.out[self.base + a:self.base + a + n].cpu().numpy().view(np.uint16)
         dist = bf16_ulp_dist(gout, ob)
-        max_ulp = max(max_ulp, int(dist.max()))
+        self.max_ulp = max(self.max_ulp, int(dist.max()))
         assert dist.max() <= BF16_ULP_BAR, f"{name} out[{a}:{a + n}]: {dist.max()} ulp"
-        nbit["out"] += int(np.count_nonzero(gout != ob))
+        self.nbit["out"] += int(np.count_nonzero(gout != ob))
         if d.mean is not None:
             gm = d.mean[a:a + n].cpu().numpy()
-            nbit["gradient"] += int(np.count_nonzero(gm.view(np.uint32) != gc.view(np.uint32)))
-    for k in ("w", "m", "v"):
-        log(f"  {name} {k}: max rel err {worst[k]:.3g}, non-bitwise {nbit[k]:,}/{V:,}")
-    log(f"  {name} out: max bf16 ulp {max_ulp}, non-bitwise {nbit['out']:,}/{V:,}")
-    if d.mean is not None:
-        log(f"  {name} stored gradient: non-bitwise {nbit['gradient']:,}/{V:,}")
-        assert nbit["gradient"] == 0, f"{name}: stored gradient bits differ"
-    return sum(nbit.values())
+            self.nbit["gradient"] += int(np.count_nonzero(gm.view(np.uint32) !=
+                                                          gc.view(np.uint32)))
+
+    def finish(self) -> int:
+        name, V = self.name, self.V
+        for k in ("w", "m", "v"):
+            log(f"  {name} {k}: max rel err {self.worst[k]:.3g}, "
+                f"non-bitwise {self.nbit[k]:,}/{V:,}")
+        log(f"  {name} out: max bf16 ulp {self.max_ulp}, non-bitwise {self.nbit['out']:,}/{V:,}")
+        if self.d.mean is not None:
+            log(f"  {name} stored gradient: non-bitwise {self.nbit['gradient']:,}/{V:,}")
+            assert self.nbit["gradient"] == 0, f"{name}: stored gradient bits differ"
+        return sum(self.nbit.values())
+
+
+def compare_unit_full(name, wl: Workload, run, unit: int, t: int, g, coef,
+                      chunk: int = 1 << 24):
+    """Every element of one unit's step against the oracle (_FullCompare),
+    from the oracle's whole gradient `g` (fp32[V], from
+    oracle_sqnorm_chunked(keep_all=True)).  Returns the number of elements
+    that are not bit-identical (all arrays)."""
+    fc = _FullCompare(name, wl, run, unit, t, coef)
+    for a in range(0, fc.V, chunk):
+        fc.chunk(a, g[a:a + min(chunk, fc.V - a)])
+    return fc.finish()
+
+
+def compare_unit_streamed(name, wl: Workload, run, unit: int, t: int, coef,
+                          chunk: int = 1 << 24):
+    """compare_unit_full without the whole gradient in host memory: the
+    oracle's gradient is drawn by the host generator and reduced chunk by
+    chunk (the next chunk drawn while this one is reduced and compared), its
+    exact squared norm accumulated, and each chunk's step compared at once.
+    `coef` must come from the whole unit's squared norm known beforehand.
+    Returns (the oracle's exactly rounded squared norm over the unit, the
+    number of elements that are not bit-identical)."""
+    fc = _FullCompare(name, wl, run, unit, t, coef)
+    acc = O.SqAcc()
+    start, n = fc.off, fc.V
+    starts = list(range(0, n, chunk))
+
+    def gen(a):
+        return [host_slices(wl, unit, t, start + a, min(chunk, n - a), j)
+                for j in range(wl.micro_batches)]
+
+    with ThreadPoolExecutor(max_workers=1) as ex:
+        fut = ex.submit(gen, starts[0]) if starts else None
+        for ci, a in enumerate(starts):
+            sls = fut.result()
+            if ci + 1 < len(starts):
+                fut = ex.submit(gen, starts[ci + 1])
+            g = oracle_gradient(wl, lambda j: sls[j])
+            del sls
+            acc.add(g)
+            fc.chunk(a, g)
+            if ci % 8 == 7:
+                log(f"  {name}: oracle step compared over {a + len(g):,}/{n:,}")
+    return acc.value(), fc.finish()
 
 
 def oracle_sampled_step(wl: Workload, unit: int, t: int, shard, idx, coef):

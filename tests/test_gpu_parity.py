@@ -21,8 +21,8 @@ import zsgen
 from fsdp_sharded_optimizer_zero_amd.runner import ShardRun
 from zsgen.workloads import WORKLOADS, STREAM_MASTER
 from parity_util import (Q_REL_BAR, assert_bf16_close, assert_state_close, coef_is_robust,
-                         compare_unit_full, host_slices_at, log, oracle_full_run,
-                         oracle_sampled_step, oracle_sqnorm_chunked, rel_err,
+                         compare_unit_full, compare_unit_streamed, host_slices_at, log,
+                         oracle_full_run, oracle_sampled_step, oracle_sqnorm_chunked, rel_err,
                          sample_indices)
 
 pytestmark = pytest.mark.gpu
@@ -436,12 +436,13 @@ def _golden_q(name, wl):
 def test_zero3_70b_full_size():
     """The 70B ZeRO-3 shard over 64 ranks as configured (1.09e9 parameters,
     64 gradient slices, ~160 GB in HBM; global clip 1.0, beta2 0.95, t = 10,
-    the rank's own bf16 shard as output).  The oracle's squared norm of the
-    whole shard is a stored value (its 7e10 gradient draws take longer than
-    a test); the clipped step's w, m, v and bf16 are compared with the oracle
-    at ~1M sampled positions using the oracle's clip coefficient, and the
-    64-rank mean there bit for bit.  Then the fused 64-slice step without the
-    clip, on freshly drawn state, at the same positions."""
+    the rank's own bf16 shard as output).  The clip coefficient comes from
+    the oracle's stored squared norm of the whole shard; the clipped step's
+    w, m, v, bf16 output and 64-rank mean are then compared with the oracle
+    element by element while the oracle's gradient is drawn and reduced
+    chunk by chunk, and the exact squared norm accumulated on the way must
+    equal the stored value bit for bit.  Then the fused 64-slice step
+    without the clip, on freshly drawn state, at ~1M sampled positions."""
     import dataclasses
     wl = WORKLOADS["zero3_70b"]
     oq = _golden_q("zero3_70b", wl)
@@ -461,11 +462,13 @@ def test_zero3_70b_full_size():
     assert coef < 1, "the clip is active in this workload"
     run.update_pass(wl.t0)
     torch.cuda.synchronize()
-    idx = sample_indices(V, 1 << 20, seed=4)
-    nb = _sampled_check("zero3_70b", wl, run, 0, wl.t0, idx, coef)
+    q_live, nb = compare_unit_streamed("zero3_70b", wl, run, 0, wl.t0, coef)
+    log(f"zero3_70b: oracle Q over the whole shard, recomputed: {q_live:.17g}")
+    assert q_live == oq, "the stored squared norm is not the oracle's"
     if coef_is_robust(oq, wl.max_grad_norm):
         assert nb == 0
-    log(f"zero3_70b: clipped step (coef {coef}) matches the oracle at {idx.size:,} positions")
+    log(f"zero3_70b: clipped step (coef {coef}): {nb:,} of {V:,} elements non-bitwise")
+    idx = sample_indices(V, 1 << 20, seed=4)
     # the fused 64-slice step without the clip, from fresh state
     run.fill_state()
     wl_nc = dataclasses.replace(wl, max_grad_norm=0.0)
