@@ -188,16 +188,23 @@ class _FullCompare:
         ob = O.bf16_rne(w)
         dev = {"w": d.w[a:a + n].cpu().numpy(), "m": d.m[a:a + n].cpu().numpy(),
                "v": d.v[a:a + n].cpu().numpy()}
+        # bit-identical elements have no error: the bars are checked on the rest
         for k, ref in (("w", w), ("m", m), ("v", v)):
-            e = rel_err(dev[k], ref)
-            self.worst[k] = max(self.worst[k], float(e.max()))
-            assert e.max() <= REL_BAR, f"{name} {k}[{a}:{a + n}]: max rel err {e.max()}"
-            self.nbit[k] += int(np.count_nonzero(dev[k].view(np.uint32) != ref.view(np.uint32)))
+            diff = dev[k].view(np.uint32) != ref.view(np.uint32)
+            nd = int(np.count_nonzero(diff))
+            self.nbit[k] += nd
+            if nd:
+                e = float(rel_err(dev[k][diff], ref[diff]).max())
+                self.worst[k] = max(self.worst[k], e)
+                assert e <= REL_BAR, f"{name} {k}[{a}:{a + n}]: max rel err {e}"
         gout = d.out[self.base + a:self.base + a + n].cpu().numpy().view(np.uint16)
-        dist = bf16_ulp_dist(gout, ob)
-        self.max_ulp = max(self.max_ulp, int(dist.max()))
-        assert dist.max() <= BF16_ULP_BAR, f"{name} out[{a}:{a + n}]: {dist.max()} ulp"
-        self.nbit["out"] += int(np.count_nonzero(gout != ob))
+        diff = gout != ob
+        nd = int(np.count_nonzero(diff))
+        self.nbit["out"] += nd
+        if nd:
+            dist = int(bf16_ulp_dist(gout[diff], ob[diff]).max())
+            self.max_ulp = max(self.max_ulp, dist)
+            assert dist <= BF16_ULP_BAR, f"{name} out[{a}:{a + n}]: {dist} ulp"
         if d.mean is not None:
             gm = d.mean[a:a + n].cpu().numpy()
             self.nbit["gradient"] += int(np.count_nonzero(gm.view(np.uint32) !=
