@@ -183,28 +183,33 @@ def step_pattern_without_arithmetic(torch, run, reps=10):
     return {"params": n, "gbps": best["gbps"], **res}
 
 
-def graph_replay(torch, run, t, steps):
-    """One whole step captured into a HIP graph (after zs_init) and replayed
-    `steps` times: the rate without host launch overhead, for steps short
-    enough that launches show.  The constants of step t are frozen at
-    capture."""
+def graph_replay(torch, run, t, steps, per_graph=20):
+    """`per_graph` whole steps (t, t+1, ...) captured into one HIP graph
+    (after zs_init) and the graph replayed until at least `steps` steps ran:
+    the rate without host launch overhead, for steps short enough that
+    launches show.  Each step's constants are frozen at capture; a replay
+    repeats them on the evolving state.  A graph of one step would mostly
+    time the graph launch itself, which on this runtime costs more than a
+    few-microsecond kernel."""
     import fsdp_sharded_optimizer_zero_amd as Z
     Z.zs_init()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        run.step(t)
+        for i in range(per_graph):
+            run.step(t + i)
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
+    reps = max(1, -(-steps // per_graph))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(steps):
+    for _ in range(reps):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = e0.elapsed_time(e1) / (reps * per_graph)
     return {"ms_per_step": ms, "value": run.V * run.units / (ms / 1e3) / 1e9,
-            "unit": "G params/s", "steps": steps}
+            "unit": "G params/s", "steps": reps * per_graph, "steps_per_graph": per_graph}
 
 
 def copy_ceiling(torch, nbytes=4 << 30, reps=10):

@@ -506,6 +506,8 @@ __device__ __forceinline__ void reduce_block_contiguous(const SqArgs& a, int64_t
     const uint32_t r0 = (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
     // the block's tile of the reduced gradient (an accumulator is always stored)
     auto mean_tile = [&]() { return buffer_rsrc(a.mean_out + base * 8, kTile * 4); };
+    // the accumulator's loads go first (four accumulation passes over 875M
+    // parameters: 12.63 ms, against 12.75 ms with them after the slices')
     f32x4 c0{}, c1{};
     if constexpr (ACC != kAccNone) {
         c0 = buffer_load_f4<kCpolNt>(mean_tile(), r0 * 16);
