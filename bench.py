@@ -214,8 +214,8 @@ def graph_replay(torch, run, t, steps, per_graph=20):
 
 def copy_ceiling(torch, nbytes=4 << 30, reps=10):
     """Practical HBM bandwidth of a 16-byte-vector copy (read + write) with
-    non-temporal loads and stores, launched one-shot: the fastest copy
-    measured on MI355X."""
+    non-temporal loads and sc1 + nt stores (the streaming step's store
+    policy), launched one-shot: the fastest copy measured on MI355X."""
     lib = bench_lib()
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)

@@ -4,9 +4,11 @@
 // WRITE_SIZE counters for a kernel whose traffic is known exactly (n16 * 16
 // bytes each way); and the step's access pattern without its arithmetic
 // (zs_bench_step_pattern, below).
-// Non-temporal loads and stores, one vector per thread of a one-shot grid:
-// the fastest copy measured on MI355X (4 GiB each way: 6.49 TB/s, against
-// 6.20 with plain loads and stores; capping blocks per CU only slowed it).
+// One vector per thread of a one-shot grid, non-temporal loads, stores with
+// the sc1 and nt bits (the streaming step's store policy): the fastest copy
+// measured on MI355X (4 GiB each way: 6.60-6.63 TB/s, against 6.44 with nt
+// stores alone and 6.20 with plain loads and stores; capping blocks per CU,
+// or blocks of 64 to 1024 threads, only slowed it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,13 +16,35 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__global__ void __launch_bounds__(256) k_stream_copy(const u32x4* __restrict__ src,
-                                                     u32x4* __restrict__ dst, int64_t n16)
+// Buffer resource over one block's tile (`bytes` from base); accesses past
+// it are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(void* base, uint32_t bytes)
 {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
-         i += stride)
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+
+constexpr int kCpolNt = 2;
+constexpr int kSc1Nt = 16 | 2;
+constexpr int kCopyThreads = 256;
+
+// Block b copies vectors [b*256, b*256 + 256), then the same span one grid
+// further on while any is left (one pass for the one-shot grid the
+// benchmark launches).
+__global__ void __launch_bounds__(kCopyThreads) k_stream_copy(const u32x4* __restrict__ src,
+                                                              u32x4* __restrict__ dst, int64_t n16)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads;
+    for (int64_t b0 = static_cast<int64_t>(blockIdx.x) * kCopyThreads; b0 < n16; b0 += stride) {
+        const int64_t left = n16 - b0;
+        const uint32_t bytes = static_cast<uint32_t>((left < kCopyThreads ? left : kCopyThreads) * 16);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(const_cast<u32x4*>(src + b0), bytes);
+        const __amdgpu_buffer_rsrc_t rd = tile_rsrc(dst + b0, bytes);
+        if (threadIdx.x < left) {
+            const uint32_t off = threadIdx.x * 16u;
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCpolNt);
+            __builtin_amdgcn_raw_buffer_store_b128(x, rd, off, 0, kSc1Nt);
+        }
+    }
 }
 
 // src and dst: device, 16-byte aligned, n16 * 16 bytes each, not overlapping.
@@ -31,7 +55,7 @@ extern "C" int zs_bench_copy(const void* src, void* dst, int64_t n16, int32_t bl
     if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return -5;
     if (n16 == 0) return 0;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_stream_copy, dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL(k_stream_copy, dim3(blocks), dim3(kCopyThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                        static_cast<u32x4*>(dst), n16);
     return hipGetLastError() == hipSuccess ? 0 : -11;
@@ -42,17 +66,13 @@ extern "C" int zs_bench_copy(const void* src, void* dst, int64_t n16, int32_t bl
 // groups q0 and q0 + 64 of the wave's 512 parameters; non-temporal loads of
 // the fp32 gradient, w, m and v; stores of w, m, v and the bf16 parameters
 // through buffer resources with sc1 and nt), with three additions per
-// element in place of AdamW.  Its time is the ceiling the step's access
-// pattern allows on the same arrays; the benchmark reports it next to the
-// step.  The bf16 value stored is the high half of w (no rounding).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
-}
-
+// element in place of AdamW.  The benchmark reports its time next to the
+// step's on the same arrays: whether the arithmetic costs the step any time
+// (in one-wave blocks the step runs faster than this pattern, whose waves,
+// with nothing to compute, issue their stores in bunches).  The bf16 value
+// stored is the high half of w (no rounding).
 constexpr int kPatThreads = 64;
 constexpr int kPatTile = kPatThreads * 8;   // parameters per block
-constexpr int kSc1Nt = 16 | 2;
 
 __global__ void __launch_bounds__(kPatThreads)
     k_step_pattern(const float* __restrict__ g, float* __restrict__ w, float* __restrict__ m,
