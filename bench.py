@@ -152,9 +152,9 @@ def step_pattern_without_arithmetic(torch, run, reps=10):
     """The step's access pattern without its arithmetic (k_step_pattern), on
     the arrays of the workload's first unit: fp32 gradient, w, m, v in, w, m,
     v and the bf16 slot out, over the first multiple of 2048 parameters, in
-    one-wave blocks at six (the step's residency) and at four per CU.  GB/s
-    at 30 bytes per parameter.  It shows whether the step's arithmetic costs
-    time: at the step's residency the step runs as fast as these accesses
+    one-wave blocks of 4 parameters per lane at ten (the step's residency)
+    and at sixteen per CU.  GB/s at 30 bytes per parameter.  It shows whether
+    the step's arithmetic costs time: the step runs as fast as these accesses
     alone, or faster (its arithmetic spaces out the requests).
     Only for steps that read a stored fp32 gradient and stream (the pattern
     of the dominant kernel there); runs after the timed region and leaves the
@@ -167,7 +167,7 @@ def step_pattern_without_arithmetic(torch, run, reps=10):
     out = d.out.data_ptr() + 2 * (run.shard.shard_offset if run.wl.out_mode == "gather" else 0)
     st = torch.cuda.current_stream()
     res = {}
-    for per_cu in (6, 4):
+    for per_cu in (10, 16):
         args = (d.mean.data_ptr(), d.w.data_ptr(), d.m.data_ptr(), d.v.data_ptr(), out, n,
                 per_cu, st.cuda_stream)
         assert lib.zs_bench_step_pattern(*args) == 0

@@ -62,35 +62,29 @@ extern "C" int zs_bench_copy(const void* src, void* dst, int64_t n16, int32_t bl
 }
 
 // The step's memory pattern without its arithmetic: the accesses of a full
-// block of the streaming optimizer step (one wave, each lane the f32x4
-// groups q0 and q0 + 64 of the wave's 512 parameters; non-temporal loads of
-// the fp32 gradient, w, m and v; stores of w, m, v and the bf16 parameters
-// through buffer resources with sc1 and nt), with three additions per
-// element in place of AdamW.  The benchmark reports its time next to the
-// step's on the same arrays: whether the arithmetic costs the step any time
-// (in one-wave blocks the step runs faster than this pattern, whose waves,
-// with nothing to compute, issue their stores in bunches).  The bf16 value
-// stored is the high half of w (no rounding).
+// block of the streaming optimizer step from a stored gradient (one wave,
+// lane l the f32x4 group l of the block's 256 parameters; non-temporal loads
+// of the fp32 gradient, w, m and v; stores of w, m, v and the bf16
+// parameters through buffer resources with sc1 and nt), with three additions
+// per element in place of AdamW.  The benchmark reports its time next to
+// the step's on the same arrays: whether the arithmetic costs the step any
+// time.  The bf16 value stored is the high half of w (no rounding).
 constexpr int kPatThreads = 64;
-constexpr int kPatTile = kPatThreads * 8;   // parameters per block
+constexpr int kPatTile = kPatThreads * 4;   // parameters per block
 
 __global__ void __launch_bounds__(kPatThreads)
     k_step_pattern(const float* __restrict__ g, float* __restrict__ w, float* __restrict__ m,
                    float* __restrict__ v, uint16_t* __restrict__ out)
 {
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kPatTile;   // first parameter
-    const int64_t r0 = (threadIdx.x >> 6) * 128 + (threadIdx.x & 63);
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(g + base);
-    const f32x4* w4 = reinterpret_cast<const f32x4*>(w + base);
-    const f32x4* m4 = reinterpret_cast<const f32x4*>(m + base);
-    const f32x4* v4 = reinterpret_cast<const f32x4*>(v + base);
-    const f32x4 g0 = __builtin_nontemporal_load(g4 + r0), g1 = __builtin_nontemporal_load(g4 + r0 + 64);
-    f32x4 w0 = __builtin_nontemporal_load(w4 + r0), w1 = __builtin_nontemporal_load(w4 + r0 + 64);
-    f32x4 m0 = __builtin_nontemporal_load(m4 + r0), m1 = __builtin_nontemporal_load(m4 + r0 + 64);
-    f32x4 v0 = __builtin_nontemporal_load(v4 + r0), v1 = __builtin_nontemporal_load(v4 + r0 + 64);
-    w0 += g0; w1 += g1; m0 += g0; m1 += g1; v0 += g0; v1 += g1;
+    const int64_t q = threadIdx.x;
+    const f32x4 g0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + base) + q);
+    f32x4 w0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(w + base) + q);
+    f32x4 m0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m + base) + q);
+    f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v + base) + q);
+    w0 += g0; m0 += g0; v0 += g0;
     constexpr uint32_t kBytes = kPatTile * 4;
-    const uint32_t b0 = static_cast<uint32_t>(r0 * 16), b1 = b0 + 1024;
+    const uint32_t b0 = static_cast<uint32_t>(q * 16);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w + base, kBytes), rm = tile_rsrc(m + base, kBytes),
                                  rv = tile_rsrc(v + base, kBytes), ro = tile_rsrc(out + base, kBytes / 2);
     auto st4 = [](__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x) {
@@ -98,18 +92,15 @@ __global__ void __launch_bounds__(kPatThreads)
                          __float_as_uint(x.w)};
         __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, kSc1Nt);
     };
-    st4(rw, b0, w0); st4(rw, b1, w1);
-    st4(rm, b0, m0); st4(rm, b1, m1);
-    st4(rv, b0, v0); st4(rv, b1, v1);
-    auto hi2 = [](f32x4 x) {
-        return u32x2{(__float_as_uint(x.x) >> 16) | (__float_as_uint(x.y) & 0xFFFF0000u),
-                     (__float_as_uint(x.z) >> 16) | (__float_as_uint(x.w) & 0xFFFF0000u)};
-    };
-    __builtin_amdgcn_raw_buffer_store_b64(hi2(w0), ro, b0 / 2, 0, kSc1Nt);
-    __builtin_amdgcn_raw_buffer_store_b64(hi2(w1), ro, b1 / 2, 0, kSc1Nt);
+    st4(rw, b0, w0);
+    st4(rm, b0, m0);
+    st4(rv, b0, v0);
+    const u32x2 hi = {(__float_as_uint(w0.x) >> 16) | (__float_as_uint(w0.y) & 0xFFFF0000u),
+                      (__float_as_uint(w0.z) >> 16) | (__float_as_uint(w0.w) & 0xFFFF0000u)};
+    __builtin_amdgcn_raw_buffer_store_b64(hi, ro, b0 / 2, 0, kSc1Nt);
 }
 
-// n parameters (a positive multiple of 512, fewer than 2^31 threads' worth);
+// n parameters (a positive multiple of 256, fewer than 2^31 threads' worth);
 // g, w, m, v: device fp32[n], out: device bf16[n], 16-byte aligned.
 // per_cu: resident blocks per CU enforced by a dynamic LDS reservation (0:
 // no cap).  Returns 0, or -1 (arguments), -5 (alignment), -11 (launch).

@@ -54,25 +54,53 @@ namespace {
 // Every choice below was measured on MI355X against its alternatives
 // (interleaved repeats in one process, the workloads' real sizes).
 //
-// Threads per block of the step and the pack; each thread owns one
-// 8-parameter vector.  A streaming step (see kStepStreamBytes) runs one-wave
+// Threads per block of the step and the pack (a pack thread owns one
+// 8-parameter vector; a step thread 4 or 8 parameters, step_lane_params).
+// A streaming step (see kStepStreamBytes) runs one-wave
 // blocks: a CU slot frees as soon as its one wave is done, not when the
 // slowest wave of a larger block is.  A smaller step, whose operands the
 // Infinity Cache partly holds from one step to the next, runs 256-thread
 // blocks (15.6M parameters: 72 us, against 78 us in one-wave blocks).
 constexpr int step_threads(bool stream) { return stream ? 64 : 256; }
+// Parameters one lane of a full block owns.  A streaming step from a stored
+// gradient gives each lane 4: one 16-byte vector of every array, so a wave's
+// loads and stores are those of a plain copy (see step_per_cu for the
+// measurements).  Every other step gives each lane 8: two 16-byte vectors,
+// or the 8 bf16 values of each of the N_d gradient slices a fused step
+// reduces.
+constexpr int step_lane_params(bool stream, bool from_slices)
+{
+    return (stream && !from_slices) ? 4 : 8;
+}
+// 8-parameter vectors one block of the step covers.
+constexpr int step_vecs(bool stream, bool from_slices)
+{
+    return step_threads(stream) * step_lane_params(stream, from_slices) / 8;
+}
 constexpr int kPackThreads = 256;
 // Blocks of the step / of the clip pass that may be resident on one CU at a
 // time.  A dynamic LDS reservation enforces the cap.  Few resident waves keep
 // the window of addresses in flight narrow, which suits the HBM better than a
-// full CU when 4 to 65 arrays stream at once.  A streaming step runs six
-// one-wave blocks per CU: 4.11 ms on the 875M-parameter shard against 4.26
-// at two 256-thread blocks (the same shard, interleaved), 4.16 and 4.56 at
-// five and four (its division and square-root chain exposed), 4.15-4.50 at
-// 7-12; 4.98 against 5.34 ms on the 1.09B shard; 128- or 192-thread blocks
-// and 2 or 4 vectors per thread were slower.  A smaller step runs two
-// 256-thread blocks per CU.  The clip pass's shape is sq_shape below.
-constexpr int step_per_cu(bool stream) { return stream ? 6 : 2; }
+// full CU when 4 to 65 arrays stream at once.
+//  - A streaming step from a stored gradient (4 parameters per lane) runs ten
+//    one-wave blocks per CU: 3.92 ms on the 875M-parameter shard, against
+//    4.11 ms for the best shape with 8 parameters per lane (six one-wave
+//    blocks per CU), 3.92-3.97 at nine and eleven, 4.01-4.04 at eight and
+//    twelve, 4.09 at sixteen, 4.19 at 20-24, 4.30 and 4.71 at seven and six,
+//    4.51 uncapped; 4.86 against 5.00 ms on the 1.09B shard, 3.92 against
+//    4.02 ms for 32 FSDP units.
+//  - A streaming step from the slices (8 parameters per lane) runs six
+//    one-wave blocks per CU: 4.11 ms on the 875M shard against 4.26 at two
+//    256-thread blocks, 4.16 and 4.56 at five and four (its division and
+//    square-root chain exposed), 4.15-4.50 at 7-12; 128- or 192-thread blocks
+//    and 2 or 4 vectors per thread were slower (these measured on the
+//    stored-gradient step before it took 4 parameters per lane).
+//  - A smaller step runs two 256-thread blocks per CU.
+// The clip pass's shape is sq_shape below.
+constexpr int step_per_cu(bool stream, bool from_slices)
+{
+    return stream ? (from_slices ? 6 : 10) : 2;
+}
 // Launch shape of the clip pass.  A bf16 reduction of kSqWideNd slices or
 // more keeps enough loads in flight per thread to run 512-thread blocks at
 // one per CU (64 slices of 1.09B: 24.1 ms, against 25.0 at two per CU, 25.3
@@ -157,7 +185,7 @@ __device__ __forceinline__ int64_t block_span(int64_t b, int64_t nb, bool xcd_co
 constexpr int kFinalThreads = 1024;
 // Threads of one launch at most.  A dispatch counts its work-items in 32
 // bits, so a longer shard takes several launches, each with a grid below
-// that (2^31 threads of one 8-parameter vector cover 1.7e10 parameters).  A
+// that (2^31 threads cover 1.7e10 parameters at 8 per thread, 8.6e9 at 4).  A
 // test build lowers the limit to run the multi-launch path on small shards.
 #ifndef ZS_MAX_LAUNCH_THREADS
 #define ZS_MAX_LAUNCH_THREADS (int64_t(1) << 31)
@@ -657,28 +685,28 @@ __device__ __forceinline__ void step_one(const StepArgs& a, const StepConsts& c,
     a.out[i] = static_cast<uint16_t>(bf16_rne(w));
 }
 
-// AdamW on a lane's 8 parameters (clipped gradient when CLIP), bias
+// AdamW on a lane's N parameters (clipped gradient when CLIP), bias
 // corrections resolved.
-template <bool CLIP, bool BC1_POW2, bool BC2_POW2>
-__device__ __forceinline__ void adamw8(const StepConsts& c, float coef, const float (&g)[8],
-                                       float (&W)[8], float (&M)[8], float (&V)[8])
+template <bool CLIP, bool BC1_POW2, bool BC2_POW2, int N>
+__device__ __forceinline__ void adamw_lane(const StepConsts& c, float coef, const float (&g)[N],
+                                           float (&W)[N], float (&M)[N], float (&V)[N])
 {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < N; ++j) {
         float gj = g[j];
         if constexpr (CLIP) gj = gj * coef;
         adamw1<BC1_POW2, BC2_POW2>(c, gj, W[j], M[j], V[j]);
     }
 }
 
-// The arithmetic of one lane's 8 parameters after its loads: the clip
+// The arithmetic of one lane's N parameters after its loads: the clip
 // coefficient, then AdamW under a uniform branch on this step's bias
 // corrections.  The scheduling barriers keep every load ahead of any
 // arithmetic, so a wave waits for memory once and computes the fp64 clip
 // coefficient while its loads are in flight.
-template <bool CLIP>
-__device__ __forceinline__ void step_arith(const StepArgs& a, const float (&g)[8], float (&W)[8],
-                                           float (&M)[8], float (&V)[8])
+template <bool CLIP, int N>
+__device__ __forceinline__ void step_arith(const StepArgs& a, const float (&g)[N], float (&W)[N],
+                                           float (&M)[N], float (&V)[N])
 {
     __builtin_amdgcn_sched_barrier(0);
     float coef = 1.0f;
@@ -686,11 +714,11 @@ __device__ __forceinline__ void step_arith(const StepArgs& a, const float (&g)[8
     __builtin_amdgcn_sched_barrier(0);
     const StepConsts c = a.c;
     if (c.bc1_pow2) {
-        if (c.bc2_pow2) adamw8<CLIP, true, true>(c, coef, g, W, M, V);
-        else adamw8<CLIP, true, false>(c, coef, g, W, M, V);
+        if (c.bc2_pow2) adamw_lane<CLIP, true, true, N>(c, coef, g, W, M, V);
+        else adamw_lane<CLIP, true, false, N>(c, coef, g, W, M, V);
     } else {
-        if (c.bc2_pow2) adamw8<CLIP, false, true>(c, coef, g, W, M, V);
-        else adamw8<CLIP, false, false>(c, coef, g, W, M, V);
+        if (c.bc2_pow2) adamw_lane<CLIP, false, true, N>(c, coef, g, W, M, V);
+        else adamw_lane<CLIP, false, false, N>(c, coef, g, W, M, V);
     }
 }
 
@@ -753,6 +781,39 @@ __device__ __forceinline__ void step_block_contiguous(const StepArgs& a, int64_t
     buffer_store_u2<CPOL>(ro, b1 / 2, u32x2{pack_bf16x2(W[4], W[5]), pack_bf16x2(W[6], W[7])});
 }
 
+// A full block of the streaming step from a stored gradient: one wave, lane
+// l owns the parameters 4l..4l+3 of the block's 256, i.e. the f32x4 group
+// q = 2*base + l of every fp32 array and the 8-byte group q of the bf16 slot,
+// so every load and store instruction covers one contiguous span (1 KB of an
+// fp32 array, 512 bytes of the slot).  Non-temporal loads; stores through
+// buffer resources over the block's tile with sc1 and nt.
+template <bool CLIP>
+__device__ __forceinline__ void step_block_lane4(const StepArgs& a, int64_t base)
+{
+    static_assert(step_threads(true) == 64 && step_lane_params(true, false) == 4,
+                  "one wave, 4 parameters per lane");
+    const int64_t q = 2 * base + threadIdx.x;
+    const f32x4 x = load<true>(reinterpret_cast<const f32x4*>(a.mean) + q);
+    const f32x4 w = load<true>(reinterpret_cast<const f32x4*>(a.w) + q);
+    const f32x4 m = load<true>(reinterpret_cast<const f32x4*>(a.m) + q);
+    const f32x4 v = load<true>(reinterpret_cast<const f32x4*>(a.v) + q);
+    const float g[4] = {x.x, x.y, x.z, x.w};
+    float W[4] = {w.x, w.y, w.z, w.w};
+    float M[4] = {m.x, m.y, m.z, m.w};
+    float V[4] = {v.x, v.y, v.z, v.w};
+    step_arith<CLIP>(a, g, W, M, V);
+    constexpr uint32_t kTile = 64 * 16;   // bytes of one fp32 array in the block's tile
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + base * 8, kTile);
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(a.m + base * 8, kTile);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.v + base * 8, kTile);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(a.out + base * 8, kTile / 2);
+    const uint32_t b = threadIdx.x * 16u;
+    buffer_store_f4<kCpolSc1Nt>(rw, b, f32x4{W[0], W[1], W[2], W[3]});
+    buffer_store_f4<kCpolSc1Nt>(rm, b, f32x4{M[0], M[1], M[2], M[3]});
+    buffer_store_f4<kCpolSc1Nt>(rv, b, f32x4{V[0], V[1], V[2], V[3]});
+    buffer_store_u2<kCpolSc1Nt>(ro, b / 2, u32x2{pack_bf16x2(W[0], W[1]), pack_bf16x2(W[2], W[3])});
+}
+
 // One full vector vi of the step in the plain mapping (8 consecutive
 // parameters; the block that meets valid_len).
 template <bool FROM_SLICES, int NDT, bool CLIP, bool STREAM>
@@ -791,9 +852,12 @@ __device__ __forceinline__ void step_vector(const StepArgs& a, int64_t vi)
 // The fused step over the slot's shard_len/8 vectors: gradient (mean of the
 // slices, or the stored mean), clip, AdamW in place, bf16 cast into the
 // slot; vectors past valid_len are pads and get +0.  Block b of a launch
-// owns step_threads(STREAM) consecutive vectors (one per thread).
-// Full blocks take the contiguous lane mapping (step_block_contiguous):
-// measured against the plain one on MI355X (interleaved medians, one box),
+// owns step_vecs(STREAM, FROM_SLICES) consecutive vectors: a streaming step
+// from a stored gradient 4 parameters per lane (step_block_lane4), every
+// other step 8.
+// Full blocks with 8 parameters per lane take the contiguous lane mapping
+// (step_block_contiguous): measured against the plain one on MI355X
+// (interleaved medians, one box),
 // 4.40 vs 4.47 ms for 875M parameters, 5.33 vs 5.51 ms for 1.09B, 70 vs 75 us
 // for 15.6M.  The block that meets valid_len takes the plain path per vector.
 // STREAM: every operand is loaded non-temporally and the full blocks store
@@ -809,12 +873,18 @@ __global__ void __launch_bounds__(step_threads(STREAM)) k_step(const StepArgs a)
 {
     const int64_t nfull = a.valid_len >> 3;
     const int64_t nslot = a.shard_len >> 3;
-    constexpr int64_t kVecs = step_threads(STREAM);
+    constexpr int64_t kVecs = step_vecs(STREAM, FROM_SLICES);
     const int64_t base = a.v0 + static_cast<int64_t>(blockIdx.x) * kVecs;
     if (base + kVecs <= nfull) {
-        step_block_contiguous<FROM_SLICES, NDT, CLIP, STREAM>(a, base);
+        if constexpr (step_lane_params(STREAM, FROM_SLICES) == 4)
+            step_block_lane4<CLIP>(a, base);
+        else
+            step_block_contiguous<FROM_SLICES, NDT, CLIP, STREAM>(a, base);
         return;
     }
+    // the block that meets valid_len: one vector per thread, plain mapping
+    // (a 4-parameter-per-lane block has more threads than vectors)
+    if (threadIdx.x >= kVecs) return;
     const int64_t vi = base + threadIdx.x;
     if (vi < nfull) {
         step_vector<FROM_SLICES, NDT, CLIP, STREAM>(a, vi);
@@ -1031,7 +1101,8 @@ int launch_step_k(const StepArgs& a, int64_t blocks, hipStream_t st)
 {
     size_t lds = 0;
     const int rc =
-        lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(step_per_cu(STREAM), &lds);
+        lds_reservation<k_step<FROM_SLICES, NDT, CLIP, STREAM>>(step_per_cu(STREAM, FROM_SLICES),
+                                                                &lds);
     if (rc != ZS_OK || blocks == kPrepareOnly) return rc;
     hipLaunchKernelGGL((k_step<FROM_SLICES, NDT, CLIP, STREAM>), dim3(blocks),
                        dim3(step_threads(STREAM)), lds, st, a);
@@ -1160,13 +1231,14 @@ int enqueue_step(StepArgs a, bool from_slices, bool clip, void* stream)
         a.valid_len * (from_slices ? 2 * static_cast<int64_t>(a.n_d) + 26 : 30);
     const bool stream_loads = step_bytes >= kStepStreamBytes;
     const int threads = step_threads(stream_loads);
-    const int64_t blocks = (nvec + threads - 1) / threads;
+    const int vecs = step_vecs(stream_loads, from_slices);
+    const int64_t blocks = (nvec + vecs - 1) / vecs;
     hipStream_t st = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const int64_t cap = max_blocks(threads);
     for (int64_t b0 = 0; b0 < blocks; b0 += cap) {
         const int64_t nb = blocks - b0 < cap ? blocks - b0 : cap;
-        a.v0 = b0 * threads;
+        a.v0 = b0 * vecs;
         const int rc = launch_step(a, from_slices, clip, stream_loads, nb, st);
         if (rc != ZS_OK) return rc;
     }

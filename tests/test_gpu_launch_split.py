@@ -1,11 +1,12 @@
 """The multi-launch path of every entry point, on the small-grid test build.
 
 A dispatch counts its work-items in 32 bits, so the library splits a shard
-whose grid would be longer into several launches (from 1.7e10 parameters on:
+whose grid would be longer into several launches (from 8.6e9 parameters on:
 shards that fit the 288 GB of one MI355X once the state is small, e.g. the
 norm of a large N_d = 1 shard).  The test build libzero_shard_smallgrid.so is
 the same source with at most 65,536 threads per launch: 524,288 parameters
-per launch of the step and of the clip pass.  Shards of 1-2 million
+per launch of the clip pass and of a step with 8 parameters per lane, 262,144
+of the streaming step from a stored gradient (4 per lane).  Shards of 1-2 million
 parameters with a ragged tail then cross several launch boundaries (the last
 launch of the 64-slice clip pass has 13 blocks, so the XCD-contiguous block
 mapping meets a grid that is not a multiple of 8).  The test build also takes
