@@ -70,9 +70,10 @@ def _guard_intact(t, n):
     return bool(np.all(t.cpu().numpy().view(np.uint32)[n:] == F32_GUARD))
 
 
-def _clip_then_step(path, s, slices, w0, m0, v0, h):
+def _clip_then_step(path, s, slices, w0, m0, v0, h, reread=False):
     """shard_grad_sqnorm (mean stored) then zero_shard_step(mean_in) with the
-    build at `path`; returns the host copies of every output."""
+    build at `path`, or with `reread` the norm alone then the step from the
+    slices; returns the host copies of every output."""
     S, V, n_d = s.shard_len, s.valid_len, s.n_d
     rows = _rows(slices, S, V)
     ptrs = [rows.data_ptr() + 2 * S * r for r in range(n_d)]
@@ -82,17 +83,29 @@ def _clip_then_step(path, s, slices, w0, m0, v0, h):
     ws = torch.empty(Z.zs_workspace_bytes(s) // 8, dtype=torch.float64, device="cuda")
     sq = torch.zeros(1, dtype=torch.float64, device="cuda")
     with Z.library(path):
-        Z.shard_grad_sqnorm(s, ptrs, mean, ws, sq)
-        Z.zero_shard_step(s, h, mean_in=mean, sqnorm=sq, master=w, exp_avg=m, exp_avg_sq=v,
-                          param_out=out)
+        if reread:
+            Z.shard_grad_sqnorm(s, ptrs, None, ws, sq)
+            Z.zero_shard_step(s, h, grad_slices=ptrs, sqnorm=sq, master=w, exp_avg=m,
+                              exp_avg_sq=v, param_out=out)
+        else:
+            Z.shard_grad_sqnorm(s, ptrs, mean, ws, sq)
+            Z.zero_shard_step(s, h, mean_in=mean, sqnorm=sq, master=w, exp_avg=m,
+                              exp_avg_sq=v, param_out=out)
     torch.cuda.synchronize()
     assert all(_guard_intact(t, V) for t in (mean, w, m, v)), "wrote past valid_len"
     return dict(mean=_f32(mean, V), w=_f32(w, V), m=_f32(m, V), v=_f32(v, V),
                 out=out.cpu().numpy().view(np.uint16).copy(), q=float(sq.item()))
 
 
-@pytest.mark.parametrize("n_d,per_rank,tail", [(8, 1_600_000, 5), (64, 1_100_000, 13)])
-def test_split_clip_pass_and_step(n_d, per_rank, tail):
+@pytest.mark.parametrize("n_d,per_rank,tail,max_norm,reread", [(8, 1_600_000, 5, 1.0, False),
+                                                               (64, 1_100_000, 13, 1.0, False),
+                                                               (8, 1_600_000, 5, 0.0, False),
+                                                               (8, 1_600_000, 5, 1.0, True)])
+def test_split_clip_pass_and_step(n_d, per_rank, tail, max_norm, reread):
+    """The clip pass with the mean stored, then the step from the stored mean
+    (with the global clip, or without one: max_norm 0); or the norm alone,
+    then the clipped step from the slices (re-read schedule).  Against the
+    normal build and the oracle."""
     psi = n_d * per_rank - tail
     rank = n_d - 1                                  # the ragged last rank
     s = Z.zs_layout(psi, n_d, rank, 8, 2)
@@ -104,23 +117,26 @@ def test_split_clip_pass_and_step(n_d, per_rank, tail):
     m0 = rng.normal(0, 1e-4, V).astype(np.float32)
     v0 = np.abs(rng.normal(0, 1e-6, V)).astype(np.float32)
     zh = Z.adamw(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, step=1000,
-                 max_grad_norm=1.0)
+                 max_grad_norm=max_norm)
     oh = O.Hparams(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, step=1000,
-                   max_grad_norm=1.0)
-    log(f"split clip+step n_d={n_d} V={V} S={S}: {-(-S // PARAMS_PER_LAUNCH)} step launches")
-    small = _clip_then_step(Z.SMALLGRID_LIB_PATH, s, slices, w0, m0, v0, zh)
-    normal = _clip_then_step(Z.LIB_PATH, s, slices, w0, m0, v0, zh)
-    for k in ("mean", "w", "m", "v"):
+                   max_grad_norm=max_norm)
+    log(f"split clip+step n_d={n_d} V={V} S={S} max_norm={max_norm} reread={reread}: "
+        f"{-(-S // PARAMS_PER_LAUNCH)} step launches")
+    small = _clip_then_step(Z.SMALLGRID_LIB_PATH, s, slices, w0, m0, v0, zh, reread)
+    normal = _clip_then_step(Z.LIB_PATH, s, slices, w0, m0, v0, zh, reread)
+    for k in (("w", "m", "v") if reread else ("mean", "w", "m", "v")):
         assert np.array_equal(small[k].view(np.uint32), normal[k].view(np.uint32)), k
     assert np.array_equal(small["out"], normal["out"])
     assert small["q"] == normal["q"], "same partials in the same order"
 
     w, m, v = w0.copy(), m0.copy(), v0.copy()
     out, q, coef = O.shard_step(n_d, S, V, oh, slices, w, m, v)
-    assert np.array_equal(small["mean"].view(np.uint32),
-                          O.reduce_mean(slices).view(np.uint32))
+    if not reread:
+        assert np.array_equal(small["mean"].view(np.uint32),
+                              O.reduce_mean(slices).view(np.uint32))
     assert abs(small["q"] - q) <= Q_REL_BAR * q
-    assert coef_is_robust(q, oh.max_grad_norm), "draw another seed"
+    if max_norm > 0:
+        assert coef_is_robust(q, oh.max_grad_norm), "draw another seed"
     for k, ref in (("w", w), ("m", m), ("v", v)):
         assert np.array_equal(small[k].view(np.uint32), ref.view(np.uint32)), k
     assert np.array_equal(small["out"][base:base + S], out)
