@@ -42,8 +42,8 @@ def _empty(n, dtype, device):
 
 @dataclass
 class Unit:
-    slices: torch.Tensor       # [m, n_d, S] int16 (bf16) or float32: micro-batch j,
-                               # row r = rank r's slice, V elements used
+    slices: torch.Tensor       # [m, n_d, pitch] int16 (bf16) or float32: micro-batch
+                               # j, row r = rank r's slice, V elements used
     w: torch.Tensor
     m: torch.Tensor
     v: torch.Tensor
@@ -76,10 +76,16 @@ class ShardRun:
         if wl.stage == 0 and out_mode == ZS_OUT_GATHER:
             out_len = S
         self.out_len = out_len
+        # Rows of the simulated ranks' slices start on a 128-byte boundary
+        # (256 for fp32), as separately allocated per-rank buffers would; the
+        # shard length itself need not be a multiple of 64 (the 70B shard's
+        # 1,093,750,000 is not), and rows S elements apart would then start
+        # off a cache-line boundary.
+        self.slice_pitch = -(-S // 64) * 64
         self.units_data = []
         for _ in range(self.units):
             self.units_data.append(Unit(
-                slices=torch.empty((self.micro, nd, S),
+                slices=torch.empty((self.micro, nd, self.slice_pitch),
                                    dtype=torch.float32 if self.f32_grads else torch.int16,
                                    device=device),
                 w=_empty(V, torch.float32, device), m=_empty(V, torch.float32, device),
@@ -151,9 +157,8 @@ class ShardRun:
                      weight_decay=wl.weight_decay, step=t, max_grad_norm=wl.max_grad_norm)
 
     def slice_ptrs(self, d: Unit, j: int = 0):
-        S = self.shard.shard_len
         base = d.slices[j].data_ptr()
-        return [base + self.gsize * S * r for r in range(self.wl.n_d)]
+        return [base + self.gsize * self.slice_pitch * r for r in range(self.wl.n_d)]
 
     def reduce_pass(self, stream=None):
         if self.grouped_units:
