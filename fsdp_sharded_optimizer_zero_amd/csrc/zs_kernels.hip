@@ -857,9 +857,9 @@ __device__ __forceinline__ void step_vector(const StepArgs& a, int64_t vi)
 // other step 8.
 // Full blocks with 8 parameters per lane take the contiguous lane mapping
 // (step_block_contiguous): measured against the plain one on MI355X
-// (interleaved medians, one box),
-// 4.40 vs 4.47 ms for 875M parameters, 5.33 vs 5.51 ms for 1.09B, 70 vs 75 us
-// for 15.6M.  The block that meets valid_len takes the plain path per vector.
+// (interleaved medians, one box), 4.40 vs 4.47 ms for 875M parameters, 5.33
+// vs 5.51 ms for 1.09B, 70 vs 75 us for 15.6M.  The block that meets
+// valid_len takes the plain path per vector.
 // STREAM: every operand is loaded non-temporally and the full blocks store
 // with sc1 as well as nt.  Measured with the contiguous mapping (interleaved
 // medians, one box): the stored gradient and v non-temporal, 4.40 vs 4.62 ms
